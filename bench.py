@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of the seg_la hot path on one MI355X.
+
+One step is one pass over every entry point, each on its own synthetic batch
+already resident in HBM, launched back to back on one stream:
+  * la_prefill  long prefill: 1 request x 131072 tokens, H=64, d=128, bf16
+  * la_decode   256 requests x 1 token, H=64, bf16, pool of 512 fp32 states
+  * la_verify   128 requests x 5 chained draft tokens, H=64, bf16, pool of 256
+HIP events on that stream bracket every call inside the timed region, so each
+entry point's own rate is reported beside the step time.  `value` is the
+prefill rate in tokens/s; the decode rate (requests/s) and the verify rate
+are reported in their own objects, each with its roofline.
+
+Algorithmic traffic (bytes the method must move; bf16 I/O, fp32 state):
+  prefill: 1024 B per (token, head) for q, k, v in and o out, plus 128 KiB of
+           state read + write per (request, head)
+  decode / verify: 128 KiB of state read + write per (request, head) plus
+           1 KiB of q, k, v, o per (token, head)
+Peaks: HBM 8 TB/s, bf16 dense MFMA 2.5 PFLOP/s.
+
+The CPU baseline runs the fp64 oracle on the host cores over a bounded sample
+of the prefill workload (a subset of heads, every token), scaled to tokens/s of
+the whole workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "prefill tokens/s (MFMA %) + decode req/s (HBM GB/s %), H=64 d=128"
+D = 128
+STATE_BYTES = D * D * 4
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def prefill_bytes(T, H, B):
+    return T * H * 4 * D * 2 + B * H * 2 * STATE_BYTES
+
+
+def prefill_useful_flops(T, H, chunk=64):
+    # per (token, head): state update 2d^2, inter-chunk term 2d^2, causal-half
+    # intra-chunk terms 2*chunk*d (scores and values), with a 64-token chunk
+    return T * H * (4 * D * D + 2 * chunk * D)
+
+
+def step_bytes(B, H, tokens):
+    return B * H * 2 * STATE_BYTES + tokens * H * 4 * D * 2
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle CPU baseline (for quick local runs)")
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="heads in the CPU-baseline sample (default: one per host core, <= 64)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import linear_attention_amd as la
+    from linear_attention_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    la.load()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def io(x):
+        return torch.from_numpy(x).view(torch.int16).view(torch.bfloat16).to(dev)
+
+    t_gen = time.time()
+    wp = W.config(4)
+    wd = W.config(3)
+    wv = W.config(5)
+    log(f"inputs generated in {time.time() - t_gen:.1f} s")
+
+    def upload(wl):
+        return dict(q=io(wl.q), k=io(wl.k), v=io(wl.v), pool=torch.from_numpy(wl.pool).to(dev),
+                    cu=torch.from_numpy(wl.cu_seqlens.astype(np.int32)).to(dev),
+                    slot=torch.from_numpy(wl.slot_idx.astype(np.int32)).to(dev),
+                    slopes=torch.from_numpy(la.la_alibi_slopes(wl.num_heads, wl.layer_id,
+                                                               wl.num_layers)).to(dev))
+
+    P, Dd, V = upload(wp), upload(wd), upload(wv)
+    P["out"] = torch.empty_like(P["q"])
+    Dd["out"] = torch.empty_like(Dd["q"])
+    V["out"] = torch.empty_like(V["q"])
+    V["state_out"] = torch.empty((wv.batch, wv.num_heads, D, D), device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+
+    def run_prefill():
+        la.la_prefill(P["q"], P["k"], P["v"], P["cu"], P["pool"], P["slot"], P["slopes"],
+                      P["out"], wp.max_seqlen, stream=stream)
+
+    def run_decode():
+        la.la_decode(Dd["q"], Dd["k"], Dd["v"], Dd["pool"], Dd["slot"], Dd["slopes"], Dd["out"],
+                     stream=stream)
+
+    def run_verify():
+        la.la_verify(V["q"], V["k"], V["v"], wv.num_draft, V["pool"], V["slot"], V["slopes"],
+                     V["out"], V["state_out"], stream=stream)
+
+    calls = [("prefill", run_prefill), ("decode", run_decode), ("verify", run_verify)]
+    for _ in range(args.warmup):
+        for _, fn in calls:
+            fn()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = {name: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(K)] for name, _ in calls}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        for name, fn in calls:
+            a, b = ev[name][s]
+            a.record(stream)
+            fn()
+            b.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = {name: float(np.mean([a.elapsed_time(b) for a, b in ev[name]])) for name, _ in calls}
+    ms_min = {name: float(np.min([a.elapsed_time(b) for a, b in ev[name]])) for name, _ in calls}
+    ms_per_step = elapsed * 1000.0 / K
+
+    H = 64
+    Tp = wp.total_tokens
+    pb = prefill_bytes(Tp, H, wp.batch)
+    p_gbs = pb / (ms["prefill"] * 1e-3) / 1e9
+    p_tflops = prefill_useful_flops(Tp, H) / (ms["prefill"] * 1e-3) / 1e12
+    db = step_bytes(wd.batch, H, wd.total_tokens)
+    vb = step_bytes(wv.batch, H, wv.total_tokens)
+    d_gbs = db / (ms["decode"] * 1e-3) / 1e9
+    v_gbs = vb / (ms["verify"] * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": Tp / (ms["prefill"] * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/k/v, 0.05*N(0,1) fp32 prefix states)",
+        "config": {
+            "workload": "long prefill T=131072 H=64 d=128 bf16 (value) + decode B=256 H=64 "
+                        "pool 512 + chain verify B=128 k=5 H=64 pool 256, one call each per step",
+            "prefill": {"batch": wp.batch, "seq_len": Tp, "num_heads": H, "head_dim": D},
+            "decode": {"batch": wd.batch, "num_heads": H, "pool_slots": wd.pool_slots},
+            "verify": {"batch": wv.batch, "num_draft": wv.num_draft, "num_heads": H,
+                       "pool_slots": wv.pool_slots},
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": p_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": p_gbs / HBM_PEAK_GBS, "traffic": None,
+            "kernel": "prefill_chunked_kernel", "algorithmic_bytes": pb,
+            "avg_ms": ms["prefill"],
+            "mfma_useful_tflops": p_tflops, "mfma_useful_frac": p_tflops / BF16_PEAK_TFLOPS,
+        },
+        "decode": {
+            "value": wd.batch / (ms["decode"] * 1e-3), "unit": "req/s", "avg_ms": ms["decode"],
+            "min_ms": ms_min["decode"],
+            "roofline": {"bound": "hbm", "achieved": d_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": d_gbs / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "recurrent_kernel<bf16>", "algorithmic_bytes": db},
+        },
+        "verify": {
+            "value": wv.batch / (ms["verify"] * 1e-3), "unit": "req/s",
+            "tokens_per_s": wv.total_tokens / (ms["verify"] * 1e-3), "avg_ms": ms["verify"],
+            "min_ms": ms_min["verify"],
+            "roofline": {"bound": "hbm", "achieved": v_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": v_gbs / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "recurrent_kernel<bf16>", "algorithmic_bytes": vb},
+        },
+        "prefill_min_ms": ms_min["prefill"],
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+
+        cores = oracle.default_threads()
+        nh = args.cpu_heads or min(64, cores)
+        heads = list(range(nh))
+        slopes = oracle.alibi_slopes(H, wp.layer_id, wp.num_layers)[heads]
+        q, k, v = (np.ascontiguousarray(x[:, heads]) for x in (wp.q, wp.k, wp.v))
+        pool = np.ascontiguousarray(wp.pool[:, heads])
+        log(f"cpu baseline: oracle on {nh} heads x {Tp} tokens, {cores} threads")
+        c0 = time.perf_counter()
+        oracle.prefill(q, k, v, wp.cu_seqlens, pool, wp.slot_idx, slopes, threads=cores)
+        cpu_s = time.perf_counter() - c0
+        result["cpu_baseline"] = {
+            "value": Tp * (nh / H) / cpu_s, "unit": "tokens/s", "cores": min(cores, nh),
+            "kind": "oracle",
+            "sample": f"long-prefill workload, heads 0..{nh - 1} of {H}, all {Tp} tokens "
+                      f"({cpu_s:.1f} s); scaled by {nh}/{H} to whole-workload tokens/s",
+        }
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,140 @@
+/*
+ * linattn.h -- C ABI of the MI355X (gfx950) segmented linear attention library
+ * (liblinattn.so).
+ *
+ * Citations name the web page "SGLang Lightning Attention 能力矩阵与 seg_la
+ * 线性注意力测试覆盖深度解析" (www.2kiu.com/news/4599301) as [LA-page] and
+ * its sections by their headings.
+ *
+ * The operation ([LA-page] §独立参考实现：逐 token 递推公式, the recurrence):
+ * every request b and head h owns a d x d fp32 state S (row = key feature,
+ * column = value feature).  For each token t of the request, in order,
+ *
+ *     S   <- S * exp(-slopes[h]) + outer(k_t, v_t)
+ *     o_t  = (q_t @ S) * head_dim^-0.5
+ *
+ * The state before the first token is read from the request's slot of a state
+ * pool and the final state is written back to that slot (prefix states,
+ * same section); pool slots no request names are never written ([LA-page]
+ * §额外覆盖：mamba 状态跟踪与布局鲁棒性).
+ *
+ * Layouts (all row-major, contiguous, device memory owned by the caller):
+ *   q, k, v, out   [T, H, d]  token-major, heads interleaved; identical memory
+ *                  to the flattened [T, H*d] output ([LA-page] §生产环境不支持
+ *                  item 4).  Element type given by `dtype`; out has the same
+ *                  type as q (bf16 outputs are rounded to nearest even).
+ *   state_pool     [pool_slots, H, d, d] float32.
+ *   slot_idx       [batch] int32, distinct, in [0, pool_slots); any order.
+ *   cu_seqlens     [batch+1] int32, cu_seqlens[0] = 0, non-decreasing,
+ *                  cu_seqlens[batch] = total_tokens (packed varlen batch).
+ *   slopes         [H] float32 per-head decay rates (see la_alibi_slopes).
+ * q, k and v have the same head count H (no grouped heads, as in the
+ * reference kernel's qo_heads == kv_heads assertion, [LA-page]
+ * §输入与配置覆盖).  head_dim must be 128.
+ *
+ * Calls are asynchronous on `stream` (0 = the null stream): the library does
+ * no host synchronisation, no device-to-host reads and no allocation on these
+ * paths, and keeps no state between calls.  The inputs must not alias out,
+ * state_pool or state_out.  Overlapping calls that name the same pool slot race.
+ *
+ * Errors: every call returns an la_status and never aborts.  Host-visible
+ * arguments are validated before anything is launched.  Device-resident
+ * metadata (cu_seqlens, slot_idx) is validated on the host only when the
+ * environment variable LA_DEBUG=1 is set (that mode synchronises the stream).
+ * Without it the kernels still stay in bounds: token ranges are clamped to
+ * [0, total_tokens) and a request whose slot index is out of range gets zero
+ * output and touches no state.
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t;
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum {
+    LA_OK = 0,
+    LA_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad metadata (LA_DEBUG) */
+    LA_ERR_UNSUPPORTED = -2, /* head_dim != 128, unknown dtype, num_draft <= 0 */
+    LA_ERR_HIP = -3          /* a HIP runtime call or kernel launch failed */
+} la_status;
+
+typedef enum {
+    LA_DTYPE_BF16 = 0, /* bfloat16 q, k, v, out */
+    LA_DTYPE_F32 = 1   /* float32 q, k, v, out: computed in fp32 end to end */
+} la_dtype;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *la_status_string(la_status s);
+
+/*
+ * Per-head slopes ([LA-page] §独立参考实现, slope bullet): the ALiBi geometric
+ * sequence (Press, Smith & Lewis, ICLR 2022: for n heads a power of two,
+ * slope_i = 2^(-8(i+1)/n); otherwise the first 2^floor(log2 n) slopes of that
+ * sequence, then every other slope of the sequence for twice as many heads)
+ * times the layer factor 1 - layer_id/(num_layers-1) + 1e-5, or 1 + 1e-5 when
+ * num_layers == 1.  Computed in double, rounded once to float.
+ * slopes_host: caller-owned HOST array of num_heads floats.
+ * Errors: LA_ERR_INVALID_ARG for num_heads <= 0, num_layers <= 0,
+ * layer_id outside [0, num_layers) or a NULL pointer.
+ */
+la_status la_alibi_slopes(int num_heads, int layer_id, int num_layers, float *slopes_host);
+
+/*
+ * Packed varlen prefill ("extend") over `batch` requests holding
+ * `total_tokens` tokens in all ([LA-page] §独立参考实现 and
+ * §输入与配置覆盖).  For every request the state is read from
+ * state_pool[slot_idx[b]], advanced through the request's tokens, and written
+ * back in place; out receives every token's output.  A zero-length request is a
+ * no-op.  max_seqlen is an upper bound on any request's length (0 means every
+ * request is empty; the call then launches nothing).
+ * bf16: chunked MFMA kernel (fp32 state, bf16 hi/lo operand splits).
+ * fp32: token-recurrent fp32 kernel.
+ * Errors: LA_ERR_INVALID_ARG for NULL pointers (q/k/v/out may be NULL only when
+ * total_tokens == 0), negative sizes, batch > pool_slots or, with LA_DEBUG=1,
+ * inconsistent cu_seqlens/slot_idx; LA_ERR_UNSUPPORTED for head_dim != 128 or
+ * an unknown dtype; LA_ERR_HIP on a launch failure.
+ */
+la_status la_prefill(const void *q, const void *k, const void *v, la_dtype dtype,
+                     const int32_t *cu_seqlens, int batch, int64_t total_tokens, int max_seqlen,
+                     int num_heads, int head_dim,
+                     float *state_pool, int64_t pool_slots, const int32_t *slot_idx,
+                     const float *slopes, void *out, hipStream_t stream);
+
+/*
+ * Decode: one token per request (q, k, v, out are [batch, H, d]).  Each
+ * request's state is read, advanced by one step of the recurrence and written
+ * back in place ([LA-page] §输入与配置覆盖, the decode kernel's role).
+ * Errors as for la_prefill (no cu_seqlens).
+ */
+la_status la_decode(const void *q, const void *k, const void *v, la_dtype dtype,
+                    int batch, int num_heads, int head_dim,
+                    float *state_pool, int64_t pool_slots, const int32_t *slot_idx,
+                    const float *slopes, void *out, hipStream_t stream);
+
+/*
+ * Chain verify: request b owns the num_draft draft tokens
+ * b*num_draft .. b*num_draft+num_draft-1 of q, k, v, out ([batch*num_draft, H, d])
+ * and processes them as one chain from its pool state ([LA-page] §生产环境不支持
+ * item 3: drafts are verified as a chain, topk = 1).  Outputs are written for
+ * every draft token.  The final state goes to state_out[b] ([batch, H, d, d]
+ * float32) and the pool is left untouched; with state_out == NULL the final
+ * state is written back to the pool slot instead.
+ * Errors as for la_decode, plus LA_ERR_UNSUPPORTED for num_draft <= 0.
+ */
+la_status la_verify(const void *q, const void *k, const void *v, la_dtype dtype,
+                    int batch, int num_draft, int num_heads, int head_dim,
+                    float *state_pool, int64_t pool_slots, const int32_t *slot_idx,
+                    const float *slopes, void *out, float *state_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

@@ -1,0 +1,183 @@
+"""MI355X-native segmented linear attention (seg_la).
+
+Thin Python binding over the C ABI of ``liblinattn.so`` (declared in
+``include/linattn.h``).  The functions carry the C names and only marshal
+arguments: they check that tensors are contiguous device tensors of the right
+dtype, pass raw pointers and the current HIP stream, and raise on a non-zero
+status.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback.  PyTorch supplies device memory and streams.
+
+The library binds to the HIP runtime that PyTorch has already loaded (torch is
+imported before the library is opened), so tensors, streams and kernels share
+one runtime.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblinattn.so")
+
+LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, -1, -2, -3
+LA_DTYPE_BF16, LA_DTYPE_F32 = 0, 1
+
+EXPORTED = ("la_status_string", "la_alibi_slopes", "la_prefill", "la_decode", "la_verify")
+
+_lib = None
+
+
+class LAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {la_status_string(status)} ({status})")
+
+
+def load():
+    """Open liblinattn.so (built in-tree by ``linear_attention_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    import torch  # noqa: F401  -- load torch's HIP runtime first
+
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run linear_attention_amd.build.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, L = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    lib.la_status_string.argtypes = [I]
+    lib.la_status_string.restype = ctypes.c_char_p
+    lib.la_alibi_slopes.argtypes = [I, I, I, P]
+    lib.la_alibi_slopes.restype = I
+    lib.la_prefill.argtypes = [P, P, P, I, P, I, L, I, I, I, P, L, P, P, P, P]
+    lib.la_prefill.restype = I
+    lib.la_decode.argtypes = [P, P, P, I, I, I, I, P, L, P, P, P, P]
+    lib.la_decode.restype = I
+    lib.la_verify.argtypes = [P, P, P, I, I, I, I, I, P, L, P, P, P, P, P]
+    lib.la_verify.restype = I
+    _lib = lib
+    return lib
+
+
+def la_status_string(status: int) -> str:
+    return load().la_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != LA_OK:
+        raise LAError(status, where)
+
+
+def la_alibi_slopes(num_heads: int, layer_id: int = 0, num_layers: int = 1) -> np.ndarray:
+    """Host fp32 slopes [num_heads] (ALiBi sequence times the layer factor)."""
+    out = np.empty(max(int(num_heads), 0), dtype=np.float32)
+    _check(load().la_alibi_slopes(int(num_heads), int(layer_id), int(num_layers),
+                                  out.ctypes.data if out.size else None), "la_alibi_slopes")
+    return out
+
+
+def _ptr(t, name, dtypes, allow_none=False):
+    import torch
+
+    if t is None:
+        if allow_none:
+            return None
+        raise TypeError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.numel() and not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr() if t.numel() else None
+
+
+def _io_dtype(q):
+    import torch
+
+    return {torch.bfloat16: LA_DTYPE_BF16, torch.float32: LA_DTYPE_F32}[q.dtype]
+
+
+def _stream(t, stream):
+    import torch
+
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    dev = t.device if t.is_cuda else torch.device("cuda", torch.cuda.current_device())
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _shape(t):
+    return tuple(t.shape)
+
+
+def la_prefill(q, k, v, cu_seqlens, state_pool, slot_idx, slopes, out, max_seqlen, stream=None):
+    """Packed varlen prefill.  q, k, v, out: [T, H, 128] bf16 or fp32;
+    cu_seqlens [B+1] int32; state_pool [P, H, 128, 128] fp32 (updated in place);
+    slot_idx [B] int32; slopes [H] fp32; max_seqlen: host int >= every length."""
+    import torch
+
+    io = (torch.bfloat16, torch.float32)
+    T, H, d = _shape(q)
+    if _shape(k) != (T, H, d) or _shape(v) != (T, H, d) or _shape(out) != (T, H, d):
+        raise ValueError("q, k, v, out must share the shape [T, H, d]")
+    if not (k.dtype == v.dtype == out.dtype == q.dtype):
+        raise TypeError("q, k, v, out must share one dtype")
+    B = cu_seqlens.numel() - 1
+    if slot_idx.numel() != B:
+        raise ValueError("slot_idx must have one entry per request")
+    rc = load().la_prefill(_ptr(q, "q", io), _ptr(k, "k", io), _ptr(v, "v", io), _io_dtype(q),
+                           _ptr(cu_seqlens, "cu_seqlens", (torch.int32,)), B, T, int(max_seqlen),
+                           H, d, _ptr(state_pool, "state_pool", (torch.float32,)),
+                           state_pool.shape[0], _ptr(slot_idx, "slot_idx", (torch.int32,), True),
+                           _ptr(slopes, "slopes", (torch.float32,)), _ptr(out, "out", io),
+                           _stream(state_pool, stream))
+    _check(rc, "la_prefill")
+
+
+def la_decode(q, k, v, state_pool, slot_idx, slopes, out, stream=None):
+    """One token per request: q, k, v, out [B, H, 128]; the pool is updated in place."""
+    import torch
+
+    io = (torch.bfloat16, torch.float32)
+    B, H, d = _shape(q)
+    if _shape(k) != (B, H, d) or _shape(v) != (B, H, d) or _shape(out) != (B, H, d):
+        raise ValueError("q, k, v, out must share the shape [B, H, d]")
+    if not (k.dtype == v.dtype == out.dtype == q.dtype):
+        raise TypeError("q, k, v, out must share one dtype")
+    if slot_idx.numel() != B:
+        raise ValueError("slot_idx must have one entry per request")
+    rc = load().la_decode(_ptr(q, "q", io), _ptr(k, "k", io), _ptr(v, "v", io), _io_dtype(q), B, H,
+                          d, _ptr(state_pool, "state_pool", (torch.float32,)), state_pool.shape[0],
+                          _ptr(slot_idx, "slot_idx", (torch.int32,), True),
+                          _ptr(slopes, "slopes", (torch.float32,)), _ptr(out, "out", io),
+                          _stream(state_pool, stream))
+    _check(rc, "la_decode")
+
+
+def la_verify(q, k, v, num_draft, state_pool, slot_idx, slopes, out, state_out=None, stream=None):
+    """Chain verify: q, k, v, out [B*num_draft, H, 128]; the final states go to
+    state_out [B, H, 128, 128] (pool untouched) or, if None, back to the pool."""
+    import torch
+
+    io = (torch.bfloat16, torch.float32)
+    N, H, d = _shape(q)
+    B = slot_idx.numel()
+    if N != B * int(num_draft):
+        raise ValueError("q must hold num_draft tokens per request")
+    if _shape(k) != (N, H, d) or _shape(v) != (N, H, d) or _shape(out) != (N, H, d):
+        raise ValueError("q, k, v, out must share one shape")
+    if not (k.dtype == v.dtype == out.dtype == q.dtype):
+        raise TypeError("q, k, v, out must share one dtype")
+    if state_out is not None and _shape(state_out) != (B, H, d, d):
+        raise ValueError("state_out must be [B, H, d, d]")
+    rc = load().la_verify(_ptr(q, "q", io), _ptr(k, "k", io), _ptr(v, "v", io), _io_dtype(q), B,
+                          int(num_draft), H, d, _ptr(state_pool, "state_pool", (torch.float32,)),
+                          state_pool.shape[0], _ptr(slot_idx, "slot_idx", (torch.int32,), True),
+                          _ptr(slopes, "slopes", (torch.float32,)), _ptr(out, "out", io),
+                          _ptr(state_out, "state_out", (torch.float32,), True),
+                          _stream(state_pool, stream))
+    _check(rc, "la_verify")

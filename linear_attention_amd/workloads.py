@@ -21,9 +21,10 @@ Recipe (shared by every workload):
     state-tracking test of [LA-page] §额外覆盖 checks for untouched slots.
   * Slot indices are a seeded permutation, so slot order is non-monotonic in
     request order ([LA-page] §输入与配置覆盖, layout-robustness cases).
-Every tensor is drawn from its own counter-keyed stream
-(numpy PCG64 seeded with SeedSequence([seed, tag, index])), so one head's
-slice or one slot's state can be regenerated without drawing the rest.
+Every tensor is drawn from counter-keyed streams (numpy PCG64 seeded with
+SeedSequence([seed, tag, index]), one per block of 256 tokens or per pool
+slot), so blocks are generated in parallel and any block can be regenerated
+alone.
 """
 from __future__ import annotations
 
@@ -55,7 +56,11 @@ def bf16_round_bits(x: np.ndarray) -> np.ndarray:
     """float32 -> bfloat16 bit patterns (uint16), round to nearest, ties to even.
     Inputs here are finite normals, so no NaN/Inf handling is needed."""
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    r = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
+    r = u >> np.uint32(16)
+    r &= np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
     return r.astype(np.uint16)
 
 
@@ -64,18 +69,23 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def normal_heads(seed: int, tag: int, T: int, heads, d: int, dtype: str) -> np.ndarray:
-    """[T, len(heads), d] N(0,1) values, head h drawn from stream (seed, tag, h)."""
-    heads = list(heads)
-    out = np.empty((T, len(heads), d), dtype=np.uint16 if dtype == "bf16" else np.float32)
+TOKEN_BLOCK = 256
 
-    def one(i):
-        x = _stream(seed, tag, heads[i]).standard_normal((T, d), dtype=np.float32)
-        out[:, i, :] = bf16_round_bits(x) if dtype == "bf16" else x
 
-    if T > 0:
+def normal_tokens(seed: int, tag: int, T: int, H: int, d: int, dtype: str) -> np.ndarray:
+    """[T, H, d] N(0,1) values; tokens [256n, 256n+256) are drawn from stream
+    (seed, tag, n) in row-major order."""
+    out = np.empty((T, H, d), dtype=np.uint16 if dtype == "bf16" else np.float32)
+
+    def one(n):
+        t0, t1 = n * TOKEN_BLOCK, min(T, (n + 1) * TOKEN_BLOCK)
+        x = _stream(seed, tag, n).standard_normal((t1 - t0, H, d), dtype=np.float32)
+        out[t0:t1] = bf16_round_bits(x) if dtype == "bf16" else x
+
+    nblocks = (T + TOKEN_BLOCK - 1) // TOKEN_BLOCK
+    if nblocks:
         with ThreadPoolExecutor(_workers()) as ex:
-            list(ex.map(one, range(len(heads))))
+            list(ex.map(one, range(nblocks)))
     return out
 
 
@@ -121,13 +131,6 @@ class Workload:
     @property
     def pool_slots(self) -> int:
         return int(self.pool.shape[0])
-
-    def qkv_heads(self, heads):
-        """q, k, v restricted to `heads`, regenerated from their streams
-        (identical to slicing the full tensors)."""
-        T, d = self.total_tokens, self.head_dim
-        return tuple(normal_heads(self.seed, tag, T, heads, d, self.dtype)
-                     for tag in (_TAG_Q, _TAG_K, _TAG_V))
 
 
 def _pool(seed, P, H, d, fill_slots, zero_slots):
@@ -178,10 +181,9 @@ def make(name, kind, dtype, num_heads, lengths, pool_slots, *, head_dim=128, see
     cu = np.zeros(B + 1, dtype=np.int32)
     np.cumsum(lengths, out=cu[1:])
     T = int(cu[-1])
-    heads = range(num_heads)
-    q = normal_heads(seed, _TAG_Q, T, heads, head_dim, dtype)
-    k = normal_heads(seed, _TAG_K, T, heads, head_dim, dtype)
-    v = normal_heads(seed, _TAG_V, T, heads, head_dim, dtype)
+    q = normal_tokens(seed, _TAG_Q, T, num_heads, head_dim, dtype)
+    k = normal_tokens(seed, _TAG_K, T, num_heads, head_dim, dtype)
+    v = normal_tokens(seed, _TAG_V, T, num_heads, head_dim, dtype)
     pool = _pool(seed, pool_slots, num_heads, head_dim, fill, zero)
     return Workload(name=name, kind=kind, dtype=dtype, num_heads=num_heads, head_dim=head_dim,
                     layer_id=layer_id, num_layers=num_layers, seed=seed, lengths=lengths,

@@ -1,0 +1,143 @@
+"""C-ABI checks that need no GPU: symbols, host-side slopes, argument validation.
+
+Validation runs before any HIP call, so these calls are safe on a machine
+without a device; the non-null pointer values below are never dereferenced.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+import torch  # noqa: F401  -- the library binds to torch's HIP runtime
+
+import linear_attention_amd as la
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "linattn.h")
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(la.LIB_PATH):
+        pytest.fail("liblinattn.so is not built (run __graft_entry__.build())")
+    return la.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:la_status|const char \*|size_t)\s*\*?\s*(la_\w+)\(", text, re.M)))
+
+
+def test_header_declares_the_bound_functions():
+    assert declared_functions() == sorted(la.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", la.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r" T (la_\w+)$", out, re.M))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_single_hip_runtime_mapped(lib):
+    maps = open("/proc/self/maps").read()
+    paths = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(paths) == 1, paths
+
+
+def test_status_strings(lib):
+    for s in (la.LA_OK, la.LA_ERR_INVALID_ARG, la.LA_ERR_UNSUPPORTED, la.LA_ERR_HIP):
+        assert la.la_status_string(s).startswith("LA_")
+    assert "unknown" in la.la_status_string(17)
+
+
+@pytest.mark.parametrize("H", list(range(1, 130)))
+def test_slopes_match_oracle_bitwise(lib, H):
+    for layer_id, L in ((0, 1), (0, 4), (1, 4), (3, 4), (5, 48)):
+        np.testing.assert_array_equal(la.la_alibi_slopes(H, layer_id, L),
+                                      oracle.alibi_slopes(H, layer_id, L), err_msg=f"H={H} {layer_id}/{L}")
+
+
+def test_slopes_reject_bad_arguments(lib):
+    buf = np.zeros(4, dtype=np.float32)
+    for args in ((0, 0, 1), (4, 1, 1), (4, -1, 2), (4, 0, 0)):
+        assert lib.la_alibi_slopes(*args, buf.ctypes.data) == la.LA_ERR_INVALID_ARG
+    assert lib.la_alibi_slopes(4, 0, 1, None) == la.LA_ERR_INVALID_ARG
+
+
+def _prefill(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=la.LA_DTYPE_BF16, cu=FAKE, batch=2, T=10, max_seqlen=8,
+             H=4, d=128, pool=FAKE, P=4, slot=FAKE, slopes=FAKE, out=FAKE, stream=None)
+    a.update(kw)
+    return lib.la_prefill(a["q"], a["k"], a["v"], a["dtype"], a["cu"], a["batch"], a["T"],
+                          a["max_seqlen"], a["H"], a["d"], a["pool"], a["P"], a["slot"],
+                          a["slopes"], a["out"], a["stream"])
+
+
+def test_prefill_validation(lib):
+    E, U = la.LA_ERR_INVALID_ARG, la.LA_ERR_UNSUPPORTED
+    assert _prefill(lib, d=64) == U           # head_dim constraint
+    assert _prefill(lib, d=256) == U
+    assert _prefill(lib, dtype=5) == U
+    assert _prefill(lib, q=None) == E
+    assert _prefill(lib, out=None) == E
+    assert _prefill(lib, pool=None) == E
+    assert _prefill(lib, slot=None) == E
+    assert _prefill(lib, slopes=None) == E
+    assert _prefill(lib, cu=None) == E
+    assert _prefill(lib, batch=-1) == E
+    assert _prefill(lib, T=-1) == E
+    assert _prefill(lib, H=0) == E
+    assert _prefill(lib, max_seqlen=-1) == E
+    assert _prefill(lib, batch=5, P=4) == E   # more requests than distinct slots
+    assert _prefill(lib, P=0) == E
+    assert _prefill(lib, batch=2 ** 28, P=2 ** 30) == E  # grid too large
+    # empty work returns before any HIP call
+    assert _prefill(lib, batch=0, T=0, max_seqlen=0, q=None, k=None, v=None, out=None, cu=FAKE,
+                    slot=None) == la.LA_OK
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=la.LA_DTYPE_BF16, batch=2, H=4, d=128, pool=FAKE, P=4,
+             slot=FAKE, slopes=FAKE, out=FAKE, stream=None)
+    a.update(kw)
+    return lib.la_decode(a["q"], a["k"], a["v"], a["dtype"], a["batch"], a["H"], a["d"], a["pool"],
+                         a["P"], a["slot"], a["slopes"], a["out"], a["stream"])
+
+
+def _verify(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=la.LA_DTYPE_BF16, batch=2, nd=5, H=4, d=128, pool=FAKE,
+             P=4, slot=FAKE, slopes=FAKE, out=FAKE, so=FAKE, stream=None)
+    a.update(kw)
+    return lib.la_verify(a["q"], a["k"], a["v"], a["dtype"], a["batch"], a["nd"], a["H"], a["d"],
+                         a["pool"], a["P"], a["slot"], a["slopes"], a["out"], a["so"], a["stream"])
+
+
+def test_decode_and_verify_validation(lib):
+    E, U = la.LA_ERR_INVALID_ARG, la.LA_ERR_UNSUPPORTED
+    assert _decode(lib, d=64) == U
+    assert _decode(lib, dtype=3) == U
+    assert _decode(lib, q=None) == E
+    assert _decode(lib, batch=9, P=4) == E
+    assert _decode(lib, slopes=None) == E
+    assert _verify(lib, nd=0) == U            # chain length must be positive
+    assert _verify(lib, nd=-2) == U
+    assert _verify(lib, d=96) == U
+    assert _verify(lib, out=None) == E
+    assert _verify(lib, batch=-1) == E
+    assert _verify(lib, batch=0, q=None, k=None, v=None, out=None, slot=None) == la.LA_OK
+
+
+def test_binding_rejects_host_tensors(lib):
+    q = torch.zeros(3, 2, 128, dtype=torch.bfloat16)
+    pool = torch.zeros(2, 2, 128, 128)
+    with pytest.raises(TypeError):
+        la.la_decode(q, q, q, pool, torch.zeros(3, dtype=torch.int32), torch.zeros(2), q)
+    with pytest.raises(TypeError):
+        la.la_decode(q, q, q.float(), pool, torch.zeros(3, dtype=torch.int32), torch.zeros(2), q)

@@ -47,9 +47,9 @@ def test_config1_layout():
     assert abs(c.pool[3].std() - 0.05) < 0.005
 
 
-def test_head_slices_regenerate_identically():
-    c = w.make("t", "prefill", "bf16", 4, [33, 7], 3, seed=5)
-    q, k, v = c.qkv_heads([2, 0])
-    np.testing.assert_array_equal(q, c.q[:, [2, 0]])
-    np.testing.assert_array_equal(k, c.k[:, [2, 0]])
-    np.testing.assert_array_equal(v, c.v[:, [2, 0]])
+def test_token_blocks_regenerate_identically():
+    c = w.make("t", "prefill", "bf16", 4, [300, 7], 3, seed=5)
+    blk = w.normal_tokens(5, 1, 307, 4, 128, "bf16")
+    np.testing.assert_array_equal(blk, c.q)
+    part = w._stream(5, 1, 1).standard_normal((51, 4, 128), dtype=np.float32)
+    np.testing.assert_array_equal(w.bf16_round_bits(part), c.q[256:])
