@@ -64,6 +64,12 @@ def main():
                     help="skip the oracle CPU baseline (for quick local runs)")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads in the CPU-baseline sample (default: one per host core, <= 64)")
+    ap.add_argument("--only", choices=["prefill", "decode", "verify"], default=None,
+                    help="run one entry point only (profiling aid; the JSON line then "
+                         "reports that call alone)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain 1 GiB device-to-device copy 5 times and exit (reference "
+                         "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -80,17 +86,28 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
-    la.load()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                          "launches": 5}), flush=True)
+        return 0
+    la.load()
 
     def io(x):
         return torch.from_numpy(x).view(torch.int16).view(torch.bfloat16).to(dev)
 
     t_gen = time.time()
-    wp = W.config(4)
-    wd = W.config(3)
-    wv = W.config(5)
+    want = {args.only} if args.only else {"prefill", "decode", "verify"}
+    wp = W.config(4) if "prefill" in want else None
+    wd = W.config(3) if "decode" in want else None
+    wv = W.config(5) if "verify" in want else None
     log(f"inputs generated in {time.time() - t_gen:.1f} s")
 
     def upload(wl):
@@ -100,11 +117,14 @@ def main():
                     slopes=torch.from_numpy(la.la_alibi_slopes(wl.num_heads, wl.layer_id,
                                                                wl.num_layers)).to(dev))
 
-    P, Dd, V = upload(wp), upload(wd), upload(wv)
-    P["out"] = torch.empty_like(P["q"])
-    Dd["out"] = torch.empty_like(Dd["q"])
-    V["out"] = torch.empty_like(V["q"])
-    V["state_out"] = torch.empty((wv.batch, wv.num_heads, D, D), device=dev)
+    P = upload(wp) if wp else None
+    Dd = upload(wd) if wd else None
+    V = upload(wv) if wv else None
+    for X in (P, Dd, V):
+        if X is not None:
+            X["out"] = torch.empty_like(X["q"])
+    if V is not None:
+        V["state_out"] = torch.empty((wv.batch, wv.num_heads, D, D), device=dev)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -121,7 +141,8 @@ def main():
         la.la_verify(V["q"], V["k"], V["v"], wv.num_draft, V["pool"], V["slot"], V["slopes"],
                      V["out"], V["state_out"], stream=stream)
 
-    calls = [("prefill", run_prefill), ("decode", run_decode), ("verify", run_verify)]
+    calls = [(n, f) for n, f in (("prefill", run_prefill), ("decode", run_decode),
+                                 ("verify", run_verify)) if n in want]
     for _ in range(args.warmup):
         for _, fn in calls:
             fn()
@@ -143,6 +164,12 @@ def main():
     ms = {name: float(np.mean([a.elapsed_time(b) for a, b in ev[name]])) for name, _ in calls}
     ms_min = {name: float(np.min([a.elapsed_time(b) for a, b in ev[name]])) for name, _ in calls}
     ms_per_step = elapsed * 1000.0 / K
+
+    if args.only:
+        name = args.only
+        print(json.dumps({"only": name, "avg_ms": ms[name], "min_ms": ms_min[name],
+                          "ms_per_step": ms_per_step, "steps": K}), flush=True)
+        return 0
 
     H = 64
     Tp = wp.total_tokens
