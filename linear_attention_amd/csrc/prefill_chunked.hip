@@ -45,17 +45,28 @@ constexpr int C = 64;        // chunk length
 constexpr int VB = 32;       // state columns per workgroup
 constexpr int NVB = D / VB;  // column blocks per head
 constexpr int NT = 256;      // threads per workgroup
-constexpr int QLD = D + 8;   // row stride (elements) of the Q and K tiles
-constexpr int VLD = VB + 16; // row stride (elements) of the V tiles
+constexpr int VLD = VB + 16; // row stride (elements) of the V tiles (conflict-free for the
+                             // 4-row transposed reads: rows land 24 banks apart)
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// Q and K tiles: 64 rows of 128 elements (256 B, one pass over the 64 LDS
+// banks) with the 16-byte units of row r permuted by u -> u ^ swz(r).  swz takes
+// 16 distinct values over any 16 consecutive rows (16-byte reads of one column
+// unit from 16 rows hit distinct banks) and maps the unit pair {2m, 2m+1} of 4
+// consecutive rows to 4 distinct pairs (the 4x16 transposed reads hit
+// distinct banks).
+__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+__device__ __forceinline__ int qk_off(int r, int col) {
+    return r * D + ((((col >> 3) ^ swz(r)) << 3) | (col & 7));
+}
+
 struct Smem {
-    uint16_t q[C][QLD];
-    uint16_t k[C][QLD];
+    uint16_t q[C * D];
+    uint16_t k[C * D];
     uint16_t v[C][VLD];
     uint16_t vd_hi[C][VLD];
     uint16_t vd_lo[C][VLD];
@@ -73,10 +84,16 @@ __device__ __forceinline__ u16x4 lds4(const uint16_t *p) { return *reinterpret_c
 // Transposed 4x16 read: the 16-lane group g addresses rows row0 + 4g .. +3 and
 // columns col0 .. col0+15 of a row-major bf16 tile with row stride ld; lane
 // (g, i) receives column col0 + i of those four rows.
-__device__ __forceinline__ u16x4 ldtr(const uint16_t *tile, int ld, int row0, int col0, int g, int l16) {
-    const uint16_t *p = tile + (row0 + 4 * g + (l16 >> 2)) * ld + col0 + 4 * (l16 & 3);
+__device__ __forceinline__ u16x4 tr_at(const uint16_t *p) {
     bf16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p));
     return __builtin_bit_cast(u16x4, r);
+}
+__device__ __forceinline__ u16x4 ldtr(const uint16_t *tile, int ld, int row0, int col0, int g, int l16) {
+    return tr_at(tile + (row0 + 4 * g + (l16 >> 2)) * ld + col0 + 4 * (l16 & 3));
+}
+// the same read from a swizzled Q/K tile (col0 a multiple of 16)
+__device__ __forceinline__ u16x4 ldtr_qk(const uint16_t *tile, int row0, int col0, int g, int l16) {
+    return tr_at(tile + qk_off(row0 + 4 * g + (l16 >> 2), col0 + 4 * (l16 & 3)));
 }
 
 __device__ __forceinline__ u16x8 cat(u16x4 a, u16x4 b) {
@@ -129,15 +146,24 @@ template <> struct Tiles<2> { static constexpr int n = 2, jt[3] = {0, 0, 0}, it[
 template <> struct Tiles<3> { static constexpr int n = 2, jt[3] = {1, 1, 0}, it[3] = {2, 3, 0};
                               static constexpr int ng = 2, git[2] = {2, 3}, ga[2] = {0, 1}, gb[2] = {-1, -1}; };
 
-// One chunk for wave W: accumulate the partial O^T tiles part[it][nt] and
-// advance this wave's state rows S[mt][nt].
-// mdec[4t + r]: causal decay of score tile t element r; qdec[it]:
-// e^{-l(i+1)} for i = 16 it + l16; dc: e^{-l c}
-template <int W>
+// Decay handling.  With kF ("factored", used for 0 <= l <= 2) the state is
+// kept in the scaled frame S_m = e^{-32 l} S, the score tiles are weighted by
+// e^{l (j - 31)} and the sum of all partials is multiplied once by
+// e^{-l (i - 31)}: that is the same o_i, because
+//   e^{-l(i-j)} = e^{-l(i-31)} e^{l(j-31)}  and  e^{-l(i+1)} S = e^{-l(i-31)} S_m,
+// and every factor stays inside the fp32/bf16 exponent range for l <= 2.
+// Without kF the weights e^{-l(i-j)} and e^{-l(i+1)} are applied directly.
+
+// One chunk for wave W: produce the partial O^T tiles part[it][nt] and
+// advance this wave's state rows S[mt][nt].  mdec[4t + r]: weight of score
+// tile t element r; qdec[it]: weight of the inter term for i = 16 it + l16
+// (only used without kF); dc: e^{-l c}.
+template <int W, bool kF>
 __device__ __forceinline__ void chunk_compute(Smem &sm, const float (&mdec)[12], const float (&qdec)[4],
                                               float dc, int g, int l16, f32x4 (&S)[2][2],
                                               f32x4 (&part)[4][2]) {
     using T = Tiles<W>;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 
     // inter term over this wave's 32 state rows: O^T[v][i] = sum_k S^T[v][k] Q^T[k][i].
     // A operand (v x k) comes from the accumulators: lane (g, l16) holds
@@ -153,26 +179,26 @@ __device__ __forceinline__ void chunk_compute(Smem &sm, const float (&mdec)[12],
     }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-        const uint16_t *qrow = &sm.q[16 * it + l16][32 * W + 4 * g];
-        const u16x8 qb = cat(lds4(qrow), lds4(qrow + 16));
+        const int qr = 16 * it + l16;
+        const u16x8 qb = cat(lds4(&sm.q[qk_off(qr, 32 * W + 4 * g)]),
+                             lds4(&sm.q[qk_off(qr, 32 * W + 16 + 4 * g)]));
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mma(sa_hi[nt], qb, acc);
+            f32x4 acc = mma(sa_hi[nt], qb, z);
             acc = mma(sa_lo[nt], qb, acc);
-            part[it][nt] += acc * qdec[it];
+            part[it][nt] = kF ? acc : acc * qdec[it];
         }
     }
 
-    // causal score tiles A^T[j][i] = k_j . q_i, masked and decayed, split hi/lo
+    // causal score tiles A^T[j][i] = k_j . q_i, weighted and masked, split hi/lo
     u16x4 p_hi[3], p_lo[3];
 #pragma unroll
     for (int t = 0; t < T::n; ++t) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 acc = z;
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            acc = mma(lds8(&sm.k[16 * T::jt[t] + l16][32 * s + 8 * g]),
-                      lds8(&sm.q[16 * T::it[t] + l16][32 * s + 8 * g]), acc);
+            acc = mma(lds8(&sm.k[qk_off(16 * T::jt[t] + l16, 32 * s + 8 * g)]),
+                      lds8(&sm.q[qk_off(16 * T::it[t] + l16, 32 * s + 8 * g)]), acc);
         f32x4 p;
 #pragma unroll
         for (int r = 0; r < 4; ++r) p[r] = acc[r] * mdec[4 * t + r];
@@ -207,8 +233,8 @@ __device__ __forceinline__ void chunk_compute(Smem &sm, const float (&mdec)[12],
         u16x8 ka[2], vh[2], vl[2];
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
-            ka[mt] = cat(ldtr(&sm.k[0][0], QLD, 32 * s2, 32 * W + 16 * mt, g, l16),
-                         ldtr(&sm.k[0][0], QLD, 32 * s2 + 16, 32 * W + 16 * mt, g, l16));
+            ka[mt] = cat(ldtr_qk(sm.k, 32 * s2, 32 * W + 16 * mt, g, l16),
+                         ldtr_qk(sm.k, 32 * s2 + 16, 32 * W + 16 * mt, g, l16));
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             vh[nt] = cat(ldtr(&sm.vd_hi[0][0], VLD, 32 * s2, 16 * nt, g, l16),
@@ -226,9 +252,9 @@ __device__ __forceinline__ void chunk_compute(Smem &sm, const float (&mdec)[12],
     }
 }
 
-// per-lane causal decay of wave W's score tiles: element (t, r) is
-// (j, i) = (16 jt + 4g + r, 16 it + l16)
-template <int W>
+// per-lane weights of wave W's score tiles: element (t, r) is
+// (j, i) = (16 jt + 4g + r, 16 it + l16), zero above the diagonal
+template <int W, bool kF>
 __device__ __forceinline__ void score_decay(float lam, int g, int l16, float (&mdec)[12]) {
     using T = Tiles<W>;
 #pragma unroll
@@ -236,7 +262,8 @@ __device__ __forceinline__ void score_decay(float lam, int g, int l16, float (&m
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int j = 16 * T::jt[t] + 4 * g + r, i = 16 * T::it[t] + l16;
-            mdec[4 * t + r] = (t < T::n && j <= i) ? expf(-lam * static_cast<float>(i - j)) : 0.f;
+            const float e = kF ? static_cast<float>(j - 31) : -static_cast<float>(i - j);
+            mdec[4 * t + r] = (t < T::n && j <= i) ? expf(lam * e) : 0.f;
         }
 }
 
@@ -251,20 +278,25 @@ struct Job {
 };
 
 // Whole request for wave W of the workgroup.
-template <int W>
+template <int W, bool kF>
 __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int l16 = lane & 15, g = lane >> 4;
     const float lam = jb.lam;
     const float scale = 0.08838834764831845f;  // 128^-1/2
-    const size_t row = jb.row, hcol = jb.hcol;
+    const uint32_t row = static_cast<uint32_t>(jb.row);
     const int col0 = jb.col0;
 
     float mdec[12], qdec[4];
-    score_decay<W>(lam, g, l16, mdec);
+    score_decay<W, kF>(lam, g, l16, mdec);
 #pragma unroll
     for (int it = 0; it < 4; ++it) qdec[it] = expf(-lam * static_cast<float>(16 * it + l16 + 1));
+    // output factor of row block W (token i = 16W + l16)
+    const float fin = kF ? scale * expf(-lam * static_cast<float>(16 * W + l16 - 31)) : scale;
+    // state frame: S_m = sigma * S
+    const float sigma = kF ? expf(-32.f * lam) : 1.f;
+    const float vshift = kF ? 32.f : 0.f;
 
     // state rows 32W..32W+31 of the block: tile (mt, nt), element r is
     // S[32W + 16mt + 4g + r][col0 + 16nt + l16]
@@ -275,39 +307,64 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                S[mt][nt][r] = jb.state[(32 * W + 16 * mt + 4 * g + r) * D + col0 + 16 * nt + l16];
+                S[mt][nt][r] = sigma * jb.state[(32 * W + 16 * mt + 4 * g + r) * D + col0 + 16 * nt + l16];
 
-    // staging registers: Q/K 16-byte pieces p = tid + 256u (row p/16, piece
-    // p%16); V piece row tid/4, columns col0 + 8*(tid%4) .. +7
-    u16x8 pq[4], pk[4], pv;
-    const u16x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-    auto fetch = [&](int64_t t, int c) {
+    // staging: Q/K 16-byte pieces p = tid + 256u (row p/16, piece p%16); V
+    // piece row tid/4, columns col0 + 8*(tid%4) .. +7.  Per-lane offsets are
+    // fixed; each chunk only moves the uniform base.
+    uint32_t offqk[4];  // byte offsets
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int p = tid + NT * u;
-            const int r = p >> 4, pc = p & 15;
-            if (r < c) {
-                const size_t off = (t + r) * row + hcol + 8 * pc;
-                pq[u] = *reinterpret_cast<const u16x8 *>(jb.q + off);
-                pk[u] = *reinterpret_cast<const u16x8 *>(jb.k + off);
-            } else {
-                pq[u] = zero8;
-                pk[u] = zero8;
-            }
-        }
-        const int r = tid >> 2;
-        pv = (r < c) ? *reinterpret_cast<const u16x8 *>(jb.v + (t + r) * row + hcol + col0 + 8 * (tid & 3))
-                     : zero8;
-    };
+    for (int u = 0; u < 4; ++u) {
+        const int p = tid + NT * u;
+        offqk[u] = 2u * (static_cast<uint32_t>(p >> 4) * row + 8 * (p & 15));
+    }
+    const int vr = tid >> 2;
+    const uint32_t offv = 2u * (static_cast<uint32_t>(vr) * row + 8 * (tid & 3));
+    const uint32_t offo = 2u * (static_cast<uint32_t>(16 * W + l16) * row + 4 * g);
 
     const int64_t len = jb.len;
     const int nchunks = static_cast<int>((len + C - 1) / C);
+    const int c_last = static_cast<int>(len - static_cast<int64_t>(nchunks - 1) * C);
+    // weight of V row vr and the state decay in a full chunk and in the last one
+    const float vdec_full = expf(-lam * (static_cast<float>(C - 1 - vr) + vshift));
+    const float vdec_last = vr < c_last ? expf(-lam * (static_cast<float>(c_last - 1 - vr) + vshift)) : 0.f;
+    const float dc_full = expf(-lam * static_cast<float>(C));
+    const float dc_last = expf(-lam * static_cast<float>(c_last));
+
+    u16x8 pq[4], pk[4], pv;
+    const u16x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+    auto ld16 = [](const char *base, uint32_t off) {
+        return *reinterpret_cast<const u16x8 *>(base + off);
+    };
+    auto fetch = [&](int64_t t, int c) {
+        const char *qb = reinterpret_cast<const char *>(jb.q + t * jb.row + jb.hcol);
+        const char *kb = reinterpret_cast<const char *>(jb.k + t * jb.row + jb.hcol);
+        const char *vb = reinterpret_cast<const char *>(jb.v + t * jb.row + jb.hcol + col0);
+        if (c == C) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                pq[u] = ld16(qb, offqk[u]);
+                pk[u] = ld16(kb, offqk[u]);
+            }
+            pv = ld16(vb, offv);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bool ok = ((tid + NT * u) >> 4) < c;
+                pq[u] = ok ? ld16(qb, offqk[u]) : zero8;
+                pk[u] = ok ? ld16(kb, offqk[u]) : zero8;
+            }
+            pv = vr < c ? ld16(vb, offv) : zero8;
+        }
+    };
+
     fetch(jb.t0, static_cast<int>(len < C ? len : C));
 
     for (int ci = 0; ci < nchunks; ++ci) {
         const int64_t t = jb.t0 + static_cast<int64_t>(ci) * C;
         const int64_t rem = len - static_cast<int64_t>(ci) * C;
         const int c = static_cast<int>(rem < C ? rem : C);
+        const bool full = c == C;
 
         // stage the chunk (every wave is past the previous chunk's reads of
         // these tiles: it waited at the partial-sum barrier below)
@@ -315,13 +372,13 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
         for (int u = 0; u < 4; ++u) {
             const int p = tid + NT * u;
             const int r = p >> 4, pc = p & 15;
-            *reinterpret_cast<u16x8 *>(&sm.q[r][8 * pc]) = pq[u];
-            *reinterpret_cast<u16x8 *>(&sm.k[r][8 * pc]) = pk[u];
+            *reinterpret_cast<u16x8 *>(&sm.q[qk_off(r, 8 * pc)]) = pq[u];
+            *reinterpret_cast<u16x8 *>(&sm.k[qk_off(r, 8 * pc)]) = pk[u];
         }
         {
-            const int r = tid >> 2, pc = tid & 3;
-            const float vdec = (r < c) ? expf(-lam * static_cast<float>(c - 1 - r)) : 0.f;
-            *reinterpret_cast<u16x8 *>(&sm.v[r][8 * pc]) = pv;
+            const int pc = tid & 3;
+            const float vdec = full ? vdec_full : vdec_last;
+            *reinterpret_cast<u16x8 *>(&sm.v[vr][8 * pc]) = pv;
             f32x4 x0, x1;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -331,8 +388,8 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
             u16x4 h0, l0, h1, l1;
             split4(x0, h0, l0);
             split4(x1, h1, l1);
-            *reinterpret_cast<u16x8 *>(&sm.vd_hi[r][8 * pc]) = cat(h0, h1);
-            *reinterpret_cast<u16x8 *>(&sm.vd_lo[r][8 * pc]) = cat(l0, l1);
+            *reinterpret_cast<u16x8 *>(&sm.vd_hi[vr][8 * pc]) = cat(h0, h1);
+            *reinterpret_cast<u16x8 *>(&sm.vd_lo[vr][8 * pc]) = cat(l0, l1);
         }
         __syncthreads();
 
@@ -342,11 +399,7 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
         }
 
         f32x4 part[4][2];
-#pragma unroll
-        for (int it = 0; it < 4; ++it)
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) part[it][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        chunk_compute<W>(sm, mdec, qdec, expf(-lam * static_cast<float>(c)), g, l16, S, part);
+        chunk_compute<W, kF>(sm, mdec, qdec, full ? dc_full : dc_last, g, l16, S, part);
 
         // hand the partial O^T tiles of the other row blocks to their owners
 #pragma unroll
@@ -356,30 +409,32 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
                 for (int nt = 0; nt < 2; ++nt) sm.part[W][it][nt][lane] = part[it][nt];
         __syncthreads();
 
-        // row block W: sum the four partials and store o = scale * O.
+        // row block W: sum the four partials and store o.
         // O^T tile nt, element r: value column col0 + 16nt + 4g + r, token 16W + l16
-        const int i = 16 * W + l16;
+        char *ob = reinterpret_cast<char *>(jb.out + t * jb.row + jb.hcol + col0);
+        const bool store = full || (16 * W + l16) < c;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             f32x4 o = part[W][nt];
 #pragma unroll
             for (int src = 0; src < 4; ++src)
                 if (src != W) o += sm.part[src][W][nt][lane];
-            if (i < c) {
-                o *= scale;
+            if (store) {
+                o *= fin;
                 const uint64_t packed = (uint64_t)cvt2(o[0], o[1]) | ((uint64_t)cvt2(o[2], o[3]) << 32);
-                *reinterpret_cast<uint64_t *>(jb.out + (t + i) * row + hcol + col0 + 16 * nt + 4 * g) = packed;
+                *reinterpret_cast<uint64_t *>(ob + offo + 32 * nt) = packed;
             }
         }
     }
 
+    const float unscale = kF ? expf(32.f * lam) : 1.f;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                jb.state[(32 * W + 16 * mt + 4 * g + r) * D + col0 + 16 * nt + l16] = S[mt][nt][r];
+                jb.state[(32 * W + 16 * mt + 4 * g + r) * D + col0 + 16 * nt + l16] = S[mt][nt][r] * unscale;
 }
 
 __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
@@ -416,11 +471,18 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(
     }
     Job jb{q, k, v, out, pool + (static_cast<size_t>(slot) * num_heads + h) * (D * D), t0, len,
            row, hcol, col0, slopes[h]};
-    switch (__builtin_amdgcn_readfirstlane(tid >> 6)) {
-    case 0: run_wave<0>(sm, jb); break;
-    case 1: run_wave<1>(sm, jb); break;
-    case 2: run_wave<2>(sm, jb); break;
-    default: run_wave<3>(sm, jb); break;
+    // slopes in [0, 2] take the factored decay path (the largest ALiBi slope
+    // is below 1); anything else the explicit one
+    const bool factored = jb.lam >= 0.f && jb.lam <= 2.f;
+    switch (__builtin_amdgcn_readfirstlane(tid >> 6) + (factored ? 0 : 4)) {
+    case 0: run_wave<0, true>(sm, jb); break;
+    case 1: run_wave<1, true>(sm, jb); break;
+    case 2: run_wave<2, true>(sm, jb); break;
+    case 3: run_wave<3, true>(sm, jb); break;
+    case 4: run_wave<0, false>(sm, jb); break;
+    case 5: run_wave<1, false>(sm, jb); break;
+    case 6: run_wave<2, false>(sm, jb); break;
+    default: run_wave<3, false>(sm, jb); break;
     }
 }
 
