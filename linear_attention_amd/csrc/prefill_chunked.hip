@@ -13,7 +13,7 @@
 // output O^T (value column x token):
 //   scores   A^T = K Q^T                     16x16 causal tiles (j <= i)
 //   intra    O^T += V^T P^T,   P = A * e^{-l(i-j)}, split hi + lo
-//   inter    O^T += S_prev^T Q^T             S_prev split hi + lo, scaled by e^{-l(i+1)}
+//   inter    O^T += S_prev^T Q^T             S_prev split hi + lo, times e^{-l(i+1)}
 //   update   S = e^{-l c} S + K^T Vd,  Vd = decayed V split hi + lo
 // The hi + lo split (x = hi + lo, both bf16) keeps every operand that is not
 // an exact bf16 input to ~2^-17 relative error; without it the bf16 rounding
@@ -29,11 +29,21 @@
 //   * a balanced share of the 10 causal score tiles and their P V products,
 //   * the update of its own state rows,
 // and the four partial O^T tiles of each 16-token row block are summed through
-// LDS by the wave that stores them.  Operands that the MFMA needs with tokens
-// along the contraction (K^T, V^T, Vd) are read from token-major LDS tiles
-// with ds_read_b64_tr_b16, whose 16-lane groups return the columns of a
-// 4-row block.  The next chunk's global loads are issued before the current
-// chunk's MFMAs.
+// LDS by the wave that stores them.
+//
+// Data movement.  Q, K and V tiles are copied from global memory straight
+// into a 3-deep LDS staging ring (global_load_lds_dwordx4: lane L of a wave
+// writes 16 bytes at base + 16 L), two chunks ahead of the chunk being
+// computed, so staging costs no registers and a chunk's loads have two chunk
+// times to arrive.  Each wave waits only for its own copies of the next chunk
+// (a counted vmcnt that leaves the newest chunk's copies in flight) before the
+// barrier that publishes them.  Operands
+// that the MFMA needs with tokens along the contraction (K^T, V^T, Vd) are
+// read from the token-major tiles with ds_read_b64_tr_b16, whose 16-lane
+// groups return the columns of a 4-row block.  Tile rows are XOR-swizzled in
+// 16-byte units so that every read pattern here is free of bank conflicts.
+// Rows past the end of a short last chunk are loaded from the chunk's last
+// row (always in bounds) and given zero weight.
 #include "common.h"
 #include "launch.h"
 
@@ -45,31 +55,38 @@ constexpr int C = 64;        // chunk length
 constexpr int VB = 32;       // state columns per workgroup
 constexpr int NVB = D / VB;  // column blocks per head
 constexpr int NT = 256;      // threads per workgroup
-constexpr int VLD = VB + 16; // row stride (elements) of the V tiles (conflict-free for the
-                             // 4-row transposed reads: rows land 24 banks apart)
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Q and K tiles: 64 rows of 128 elements (256 B, one pass over the 64 LDS
-// banks) with the 16-byte units of row r permuted by u -> u ^ swz(r).  swz takes
-// 16 distinct values over any 16 consecutive rows (16-byte reads of one column
-// unit from 16 rows hit distinct banks) and maps the unit pair {2m, 2m+1} of 4
-// consecutive rows to 4 distinct pairs (the 4x16 transposed reads hit
-// distinct banks).
+// banks); the 16-byte units of row r are permuted by u -> u ^ swz(r).  swz
+// takes 16 distinct values over any 16 consecutive rows (16-byte reads of one
+// column unit from 16 rows hit distinct banks) and maps the unit pair
+// {2m, 2m+1} of 4 consecutive rows to 4 distinct pairs (the 4x16 transposed
+// reads hit distinct banks).
 __device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 __device__ __forceinline__ int qk_off(int r, int col) {
     return r * D + ((((col >> 3) ^ swz(r)) << 3) | (col & 7));
 }
+// V tiles: 64 rows of 32 elements (64 B); units permuted by u -> u ^ swv(r),
+// which moves rows 4..7 of every 8 to the other half of the banks.
+__device__ __forceinline__ int swv(int r) { return ((r >> 2) & 1) << 1; }
+__device__ __forceinline__ int v_off(int r, int col) {
+    return r * VB + ((((col >> 3) ^ swv(r)) << 3) | (col & 7));
+}
+
+constexpr int NBUF = 3;  // staging buffers: copies run two chunks ahead
 
 struct Smem {
-    uint16_t q[C * D];
-    uint16_t k[C * D];
-    uint16_t v[C][VLD];
-    uint16_t vd_hi[C][VLD];
-    uint16_t vd_lo[C][VLD];
+    uint16_t q[NBUF][C * D];  // staging ring
+    uint16_t k[NBUF][C * D];
+    uint16_t v[NBUF][C * VB];
+    uint16_t vd_hi[C * VB];   // decayed V of the current chunk, hi/lo
+    uint16_t vd_lo[C * VB];
     f32x4 part[4][4][2][64];  // [source wave][row block][column tile][lane]
 };
 
@@ -82,18 +99,31 @@ __device__ __forceinline__ u16x8 lds8(const uint16_t *p) { return *reinterpret_c
 __device__ __forceinline__ u16x4 lds4(const uint16_t *p) { return *reinterpret_cast<const u16x4 *>(p); }
 
 // Transposed 4x16 read: the 16-lane group g addresses rows row0 + 4g .. +3 and
-// columns col0 .. col0+15 of a row-major bf16 tile with row stride ld; lane
-// (g, i) receives column col0 + i of those four rows.
+// columns col0 .. col0+15 (col0 a multiple of 16); lane (g, i) receives
+// column col0 + i of those four rows.
+//
+// The read is issued as inline assembly: the compiler cannot tell these LDS
+// reads apart from the in-flight global->LDS copies into other staging slots
+// and would otherwise wait for every outstanding copy before each of them.
+// The caller publishes the results with lds_fence(): a wait on the LDS
+// counter followed by an empty asm per value, which orders every consumer
+// after the wait.  (LDS operations complete in order, so the extra
+// outstanding reads only make the compiler's own LDS waits more conservative.)
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void *)p));
+}
 __device__ __forceinline__ u16x4 tr_at(const uint16_t *p) {
-    bf16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4 *)(p));
+    uint64_t r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
     return __builtin_bit_cast(u16x4, r);
 }
-__device__ __forceinline__ u16x4 ldtr(const uint16_t *tile, int ld, int row0, int col0, int g, int l16) {
-    return tr_at(tile + (row0 + 4 * g + (l16 >> 2)) * ld + col0 + 4 * (l16 & 3));
-}
-// the same read from a swizzled Q/K tile (col0 a multiple of 16)
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void pin(u16x8 &x) { asm volatile("" : "+v"(x)); }
 __device__ __forceinline__ u16x4 ldtr_qk(const uint16_t *tile, int row0, int col0, int g, int l16) {
     return tr_at(tile + qk_off(row0 + 4 * g + (l16 >> 2), col0 + 4 * (l16 & 3)));
+}
+__device__ __forceinline__ u16x4 ldtr_v(const uint16_t *tile, int row0, int col0, int g, int l16) {
+    return tr_at(tile + v_off(row0 + 4 * g + (l16 >> 2), col0 + 4 * (l16 & 3)));
 }
 
 __device__ __forceinline__ u16x8 cat(u16x4 a, u16x4 b) {
@@ -133,18 +163,33 @@ __device__ __forceinline__ void map_block(int id, int pairs, int &pair, int &vb)
     }
 }
 
-// Score tiles (j-tile, i-tile), j <= i, dealt to the waves 3/3/2/2; each
-// wave's P V products group its tiles by i-tile (at most two j-tiles, which
-// together fill one 32-token contraction).
+// Score tiles (j-tile, i-tile), j <= i, dealt to the waves 3/3/2/2.  Each
+// wave loads the K fragments of its distinct j-tiles (jl) and the Q fragments
+// of its distinct i-tiles (il) once; tile t uses jl[tj[t]] and il[ti[t]].  The
+// P V products group a wave's tiles by i-tile (at most two j-tiles, which
+// together fill one 32-token contraction): group q covers i-tile git[q] with
+// tiles ga[q] and gb[q] (-1: none).
 template <int W> struct Tiles;
-template <> struct Tiles<0> { static constexpr int n = 3, jt[3] = {0, 0, 1}, it[3] = {0, 1, 1};
-                              static constexpr int ng = 2, git[2] = {0, 1}, ga[2] = {0, 1}, gb[2] = {-1, 2}; };
-template <> struct Tiles<1> { static constexpr int n = 3, jt[3] = {2, 2, 3}, it[3] = {2, 3, 3};
-                              static constexpr int ng = 2, git[2] = {2, 3}, ga[2] = {0, 1}, gb[2] = {-1, 2}; };
-template <> struct Tiles<2> { static constexpr int n = 2, jt[3] = {0, 0, 0}, it[3] = {2, 3, 0};
-                              static constexpr int ng = 2, git[2] = {2, 3}, ga[2] = {0, 1}, gb[2] = {-1, -1}; };
-template <> struct Tiles<3> { static constexpr int n = 2, jt[3] = {1, 1, 0}, it[3] = {2, 3, 0};
-                              static constexpr int ng = 2, git[2] = {2, 3}, ga[2] = {0, 1}, gb[2] = {-1, -1}; };
+template <> struct Tiles<0> {
+    static constexpr int n = 3, tj[3] = {0, 0, 1}, ti[3] = {0, 1, 1};
+    static constexpr int nj = 2, jl[2] = {0, 1}, ni = 2, il[2] = {0, 1};
+    static constexpr int ng = 2, git[2] = {0, 1}, ga[2] = {0, 1}, gb[2] = {-1, 2};
+};
+template <> struct Tiles<1> {
+    static constexpr int n = 3, tj[3] = {0, 0, 1}, ti[3] = {0, 1, 1};
+    static constexpr int nj = 2, jl[2] = {2, 3}, ni = 2, il[2] = {2, 3};
+    static constexpr int ng = 2, git[2] = {2, 3}, ga[2] = {0, 1}, gb[2] = {-1, 2};
+};
+template <> struct Tiles<2> {
+    static constexpr int n = 2, tj[3] = {0, 0, 0}, ti[3] = {0, 1, 0};
+    static constexpr int nj = 1, jl[2] = {0, 0}, ni = 2, il[2] = {2, 3};
+    static constexpr int ng = 2, git[2] = {2, 3}, ga[2] = {0, 1}, gb[2] = {-1, -1};
+};
+template <> struct Tiles<3> {
+    static constexpr int n = 2, tj[3] = {0, 0, 0}, ti[3] = {0, 1, 0};
+    static constexpr int nj = 1, jl[2] = {1, 1}, ni = 2, il[2] = {2, 3};
+    static constexpr int ng = 2, git[2] = {2, 3}, ga[2] = {0, 1}, gb[2] = {-1, -1};
+};
 
 // Decay handling.  With kF ("factored", used for 0 <= l <= 2) the state is
 // kept in the scaled frame S_m = e^{-32 l} S, the score tiles are weighted by
@@ -158,16 +203,41 @@ template <> struct Tiles<3> { static constexpr int n = 2, jt[3] = {1, 1, 0}, it[
 // advance this wave's state rows S[mt][nt].  mdec[4t + r]: weight of score
 // tile t element r; qdec[it]: weight of the inter term for i = 16 it + l16
 // (only used without kF); dc: e^{-l c}.
+//
+// The work is laid out in stages separated by scheduling barriers so that
+// every group of LDS fragment reads is issued well before the MFMAs that
+// consume it: its latency is covered by VALU work (state and score splits)
+// or by the previous group's MFMAs.
 template <int W, bool kF>
-__device__ __forceinline__ void chunk_compute(Smem &sm, const float (&mdec)[12], const float (&qdec)[4],
-                                              float dc, int g, int l16, f32x4 (&S)[2][2],
-                                              f32x4 (&part)[4][2]) {
+__device__ __forceinline__ void chunk_compute(const uint16_t *sq, const uint16_t *sk, const uint16_t *sv,
+                                              const uint16_t *svh, const uint16_t *svl,
+                                              const float (&mdec)[12], const float (&qdec)[4], float dc,
+                                              int g, int l16, f32x4 (&S)[2][2], f32x4 (&part)[4][2]) {
     using T = Tiles<W>;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const u16x4 z4 = {0, 0, 0, 0};
 
-    // inter term over this wave's 32 state rows: O^T[v][i] = sum_k S^T[v][k] Q^T[k][i].
-    // A operand (v x k) comes from the accumulators: lane (g, l16) holds
-    // rows k = 32W + 4g + r (mt 0) and 32W + 16 + 4g + r (mt 1) of column v = l16.
+    // stage 1: fragments of the inter term (Q^T restricted to this wave's 32
+    // state rows, all four row blocks) and of the score tiles
+    u16x8 qb[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int qr = 16 * it + l16;
+        qb[it] = cat(lds4(&sq[qk_off(qr, 32 * W + 4 * g)]), lds4(&sq[qk_off(qr, 32 * W + 16 + 4 * g)]));
+    }
+    u16x8 kf[2][4], qf[2][4];
+#pragma unroll
+    for (int a = 0; a < T::nj; ++a)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kf[a][s] = lds8(&sk[qk_off(16 * T::jl[a] + l16, 32 * s + 8 * g)]);
+#pragma unroll
+    for (int b = 0; b < T::ni; ++b)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qf[b][s] = lds8(&sq[qk_off(16 * T::il[b] + l16, 32 * s + 8 * g)]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // stage 2: the state as bf16 hi/lo A operand (v x k): lane (g, l16) holds
+    // rows k = 32W + 4g + r (mt 0) and 32W + 16 + 4g + r (mt 1) of column v = l16
     u16x8 sa_hi[2], sa_lo[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -177,36 +247,79 @@ __device__ __forceinline__ void chunk_compute(Smem &sm, const float (&mdec)[12],
         sa_hi[nt] = cat(h0, h1);
         sa_lo[nt] = cat(l0, l1);
     }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // stage 3: inter term O^T[v][i] = sum_k S^T[v][k] Q^T[k][i] over this wave's rows
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int qr = 16 * it + l16;
-        const u16x8 qb = cat(lds4(&sm.q[qk_off(qr, 32 * W + 4 * g)]),
-                             lds4(&sm.q[qk_off(qr, 32 * W + 16 + 4 * g)]));
+    for (int it = 0; it < 4; ++it)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-            f32x4 acc = mma(sa_hi[nt], qb, z);
-            acc = mma(sa_lo[nt], qb, acc);
+            f32x4 acc = mma(sa_hi[nt], qb[it], z);
+            acc = mma(sa_lo[nt], qb[it], acc);
             part[it][nt] = kF ? acc : acc * qdec[it];
         }
-    }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // causal score tiles A^T[j][i] = k_j . q_i, weighted and masked, split hi/lo
+    // stage 4: issue the V^T fragments of the P V products and the first half
+    // of the state-update fragments, then the score MFMAs
+    u16x8 av[2][2];
+#pragma unroll
+    for (int q = 0; q < T::ng; ++q) {
+        const int ta = T::ga[q], tb = T::gb[q];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+            av[q][nt] = cat(ldtr_v(sv, 16 * T::jl[T::tj[ta]], 16 * nt, g, l16),
+                            tb >= 0 ? ldtr_v(sv, 16 * T::jl[T::tj[tb]], 16 * nt, g, l16) : z4);
+    }
+    u16x8 ka[2][2], vh[2][2], vl[2][2];
+    auto kv_frags = [&](int s2) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+            ka[s2][mt] = cat(ldtr_qk(sk, 32 * s2, 32 * W + 16 * mt, g, l16),
+                             ldtr_qk(sk, 32 * s2 + 16, 32 * W + 16 * mt, g, l16));
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            vh[s2][nt] = cat(ldtr_v(svh, 32 * s2, 16 * nt, g, l16), ldtr_v(svh, 32 * s2 + 16, 16 * nt, g, l16));
+            vl[s2][nt] = cat(ldtr_v(svl, 32 * s2, 16 * nt, g, l16), ldtr_v(svl, 32 * s2 + 16, 16 * nt, g, l16));
+        }
+    };
+    kv_frags(0);
+    f32x4 sc[3];
+#pragma unroll
+    for (int t = 0; t < T::n; ++t) sc[t] = z;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int t = 0; t < T::n; ++t) sc[t] = mma(kf[T::tj[t]][s], qf[T::ti[t]][s], sc[t]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // stage 5: weight, mask and split the scores (A^T[j][i] = k_j . q_i)
     u16x4 p_hi[3], p_lo[3];
 #pragma unroll
     for (int t = 0; t < T::n; ++t) {
-        f32x4 acc = z;
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            acc = mma(lds8(&sm.k[qk_off(16 * T::jt[t] + l16, 32 * s + 8 * g)]),
-                      lds8(&sm.q[qk_off(16 * T::it[t] + l16, 32 * s + 8 * g)]), acc);
         f32x4 p;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = acc[r] * mdec[4 * t + r];
+        for (int r = 0; r < 4; ++r) p[r] = sc[t][r] * mdec[4 * t + r];
         split4(p, p_hi[t], p_lo[t]);
     }
-    // intra term O^T[v][i] += sum_j V[j][v] P[i][j]; B operand slots 0..3 hold
-    // j-tile ga's rows 4g..4g+3, slots 4..7 j-tile gb's (or zero)
-    const u16x4 z4 = {0, 0, 0, 0};
+    __builtin_amdgcn_sched_barrier(0);
+
+    // stage 6: intra term O^T[v][i] += sum_j V[j][v] P[i][j]; B operand slots
+    // 0..3 hold j-tile ga's rows 4g..4g+3, slots 4..7 j-tile gb's (or zero).
+    // The V^T fragments and the first half of the state-update fragments are
+    // published, then the second half is issued.
+    lds_wait();
+#pragma unroll
+    for (int q = 0; q < T::ng; ++q)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) pin(av[q][nt]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        pin(ka[0][i]);
+        pin(vh[0][i]);
+        pin(vl[0][i]);
+    }
+    kv_frags(1);
 #pragma unroll
     for (int q = 0; q < T::ng; ++q) {
         const int ta = T::ga[q], tb = T::gb[q];
@@ -215,56 +328,59 @@ __device__ __forceinline__ void chunk_compute(Smem &sm, const float (&mdec)[12],
         const u16x8 bl = cat(p_lo[ta], tb >= 0 ? p_lo[tb] : z4);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-            const u16x4 va = ldtr(&sm.v[0][0], VLD, 16 * T::jt[ta], 16 * nt, g, l16);
-            const u16x4 vb = tb >= 0 ? ldtr(&sm.v[0][0], VLD, 16 * T::jt[tb], 16 * nt, g, l16) : z4;
-            const u16x8 av = cat(va, vb);
-            part[it][nt] = mma(av, bh, part[it][nt]);
-            part[it][nt] = mma(av, bl, part[it][nt]);
+            part[it][nt] = mma(av[q][nt], bh, part[it][nt]);
+            part[it][nt] = mma(av[q][nt], bl, part[it][nt]);
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // state update of rows 32W..32W+31: S[k][v] = e^{-l c} S + sum_j K[j][k] Vd[j][v]
+    // stage 7: state update of rows 32W..32W+31:
+    // S[k][v] = e^{-l c} S + sum_j K[j][k] Vd[j][v]
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) S[mt][nt] *= dc;
+    lds_wait();
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-        u16x8 ka[2], vh[2], vl[2];
+    for (int i = 0; i < 2; ++i) {
+        pin(ka[1][i]);
+        pin(vh[1][i]);
+        pin(vl[1][i]);
+    }
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-            ka[mt] = cat(ldtr_qk(sm.k, 32 * s2, 32 * W + 16 * mt, g, l16),
-                         ldtr_qk(sm.k, 32 * s2 + 16, 32 * W + 16 * mt, g, l16));
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            vh[nt] = cat(ldtr(&sm.vd_hi[0][0], VLD, 32 * s2, 16 * nt, g, l16),
-                         ldtr(&sm.vd_hi[0][0], VLD, 32 * s2 + 16, 16 * nt, g, l16));
-            vl[nt] = cat(ldtr(&sm.vd_lo[0][0], VLD, 32 * s2, 16 * nt, g, l16),
-                         ldtr(&sm.vd_lo[0][0], VLD, 32 * s2 + 16, 16 * nt, g, l16));
-        }
+    for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-                S[mt][nt] = mma(ka[mt], vh[nt], S[mt][nt]);
-                S[mt][nt] = mma(ka[mt], vl[nt], S[mt][nt]);
+                S[mt][nt] = mma(ka[s2][mt], vh[s2][nt], S[mt][nt]);
+                S[mt][nt] = mma(ka[s2][mt], vl[s2][nt], S[mt][nt]);
             }
-    }
 }
 
 // per-lane weights of wave W's score tiles: element (t, r) is
-// (j, i) = (16 jt + 4g + r, 16 it + l16), zero above the diagonal
+// (j, i) = (16 jt + 4g + r, 16 it + l16), zero above the diagonal and for
+// key rows j >= c (past the end of a short chunk)
 template <int W, bool kF>
-__device__ __forceinline__ void score_decay(float lam, int g, int l16, float (&mdec)[12]) {
+__device__ __forceinline__ void score_weights(float lam, int g, int l16, int c, float (&mdec)[12]) {
     using T = Tiles<W>;
 #pragma unroll
     for (int t = 0; t < 3; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int j = 16 * T::jt[t] + 4 * g + r, i = 16 * T::it[t] + l16;
+            const int j = 16 * T::jl[T::tj[t]] + 4 * g + r, i = 16 * T::il[T::ti[t]] + l16;
             const float e = kF ? static_cast<float>(j - 31) : -static_cast<float>(i - j);
-            mdec[4 * t + r] = (t < T::n && j <= i) ? expf(lam * e) : 0.f;
+            mdec[4 * t + r] = (t < T::n && j <= i && j < c) ? expf(lam * e) : 0.f;
         }
+}
+
+// Workgroup barrier for LDS data only.  __syncthreads() would also wait for
+// every outstanding global->LDS copy (it is a release fence); the copies are
+// waited for explicitly with counted vmcnt waits instead.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 struct Job {
@@ -288,8 +404,13 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
     const uint32_t row = static_cast<uint32_t>(jb.row);
     const int col0 = jb.col0;
 
-    float mdec[12], qdec[4];
-    score_decay<W, kF>(lam, g, l16, mdec);
+    const int64_t len = jb.len;
+    const int nchunks = static_cast<int>((len + C - 1) / C);
+    const int c_last = static_cast<int>(len - static_cast<int64_t>(nchunks - 1) * C);
+
+    float mdec[12], mdec_last[12], qdec[4];
+    score_weights<W, kF>(lam, g, l16, C, mdec);
+    score_weights<W, kF>(lam, g, l16, c_last, mdec_last);
 #pragma unroll
     for (int it = 0; it < 4; ++it) qdec[it] = expf(-lam * static_cast<float>(16 * it + l16 + 1));
     // output factor of row block W (token i = 16W + l16)
@@ -309,97 +430,97 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
             for (int r = 0; r < 4; ++r)
                 S[mt][nt][r] = sigma * jb.state[(32 * W + 16 * mt + 4 * g + r) * D + col0 + 16 * nt + l16];
 
-    // staging: Q/K 16-byte pieces p = tid + 256u (row p/16, piece p%16); V
-    // piece row tid/4, columns col0 + 8*(tid%4) .. +7.  Per-lane offsets are
-    // fixed; each chunk only moves the uniform base.
-    uint32_t offqk[4];  // byte offsets
+    // Async staging.  Wave W copies Q/K rows 16W..16W+15 (4 instructions of
+    // 4 rows each) and V rows 16W..16W+15 (one instruction); lane L of a copy
+    // fills LDS unit L of its 1 KB block, so it loads the logical unit that
+    // the swizzle places there.
+    int qk_row[4], qk_unit[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int p = tid + NT * u;
-        offqk[u] = 2u * (static_cast<uint32_t>(p >> 4) * row + 8 * (p & 15));
+        qk_row[u] = 16 * W + 4 * u + (lane >> 4);
+        qk_unit[u] = (lane & 15) ^ swz(qk_row[u]);
     }
-    const int vr = tid >> 2;
-    const uint32_t offv = 2u * (static_cast<uint32_t>(vr) * row + 8 * (tid & 3));
-    const uint32_t offo = 2u * (static_cast<uint32_t>(16 * W + l16) * row + 4 * g);
-
-    const int64_t len = jb.len;
-    const int nchunks = static_cast<int>((len + C - 1) / C);
-    const int c_last = static_cast<int>(len - static_cast<int64_t>(nchunks - 1) * C);
-    // weight of V row vr and the state decay in a full chunk and in the last one
-    const float vdec_full = expf(-lam * (static_cast<float>(C - 1 - vr) + vshift));
-    const float vdec_last = vr < c_last ? expf(-lam * (static_cast<float>(c_last - 1 - vr) + vshift)) : 0.f;
-    const float dc_full = expf(-lam * static_cast<float>(C));
-    const float dc_last = expf(-lam * static_cast<float>(c_last));
-
-    u16x8 pq[4], pk[4], pv;
-    const u16x8 zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
-    auto ld16 = [](const char *base, uint32_t off) {
-        return *reinterpret_cast<const u16x8 *>(base + off);
-    };
-    auto fetch = [&](int64_t t, int c) {
-        const char *qb = reinterpret_cast<const char *>(jb.q + t * jb.row + jb.hcol);
-        const char *kb = reinterpret_cast<const char *>(jb.k + t * jb.row + jb.hcol);
-        const char *vb = reinterpret_cast<const char *>(jb.v + t * jb.row + jb.hcol + col0);
-        if (c == C) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                pq[u] = ld16(qb, offqk[u]);
-                pk[u] = ld16(kb, offqk[u]);
-            }
-            pv = ld16(vb, offv);
-        } else {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const bool ok = ((tid + NT * u) >> 4) < c;
-                pq[u] = ok ? ld16(qb, offqk[u]) : zero8;
-                pk[u] = ok ? ld16(kb, offqk[u]) : zero8;
-            }
-            pv = vr < c ? ld16(vb, offv) : zero8;
-        }
-    };
-
-    fetch(jb.t0, static_cast<int>(len < C ? len : C));
-
-    for (int ci = 0; ci < nchunks; ++ci) {
-        const int64_t t = jb.t0 + static_cast<int64_t>(ci) * C;
-        const int64_t rem = len - static_cast<int64_t>(ci) * C;
-        const int c = static_cast<int>(rem < C ? rem : C);
-        const bool full = c == C;
-
-        // stage the chunk (every wave is past the previous chunk's reads of
-        // these tiles: it waited at the partial-sum barrier below)
+    const int v_row = 16 * W + (lane >> 2);
+    const int v_unit = (lane & 3) ^ swv(v_row);
+    auto issue_copies = [&](int64_t t, int c, int buf) {
+        const uint16_t *qb = jb.q + t * jb.row + jb.hcol;
+        const uint16_t *kb = jb.k + t * jb.row + jb.hcol;
+        const uint16_t *vb = jb.v + t * jb.row + jb.hcol + col0;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int p = tid + NT * u;
-            const int r = p >> 4, pc = p & 15;
-            *reinterpret_cast<u16x8 *>(&sm.q[qk_off(r, 8 * pc)]) = pq[u];
-            *reinterpret_cast<u16x8 *>(&sm.k[qk_off(r, 8 * pc)]) = pk[u];
+            const int r = qk_row[u] < c ? qk_row[u] : c - 1;
+            const uint32_t off = static_cast<uint32_t>(r) * row + 8 * qk_unit[u];
+            const int dst = (16 * W + 4 * u) * D;
+            __builtin_amdgcn_global_load_lds(qb + off, (lds_void *)&sm.q[buf][dst], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(kb + off, (lds_void *)&sm.k[buf][dst], 16, 0, 0);
         }
-        {
-            const int pc = tid & 3;
-            const float vdec = full ? vdec_full : vdec_last;
-            *reinterpret_cast<u16x8 *>(&sm.v[vr][8 * pc]) = pv;
-            f32x4 x0, x1;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                x0[e] = bf16_to_f32(pv[e]) * vdec;
-                x1[e] = bf16_to_f32(pv[4 + e]) * vdec;
-            }
-            u16x4 h0, l0, h1, l1;
-            split4(x0, h0, l0);
-            split4(x1, h1, l1);
-            *reinterpret_cast<u16x8 *>(&sm.vd_hi[vr][8 * pc]) = cat(h0, h1);
-            *reinterpret_cast<u16x8 *>(&sm.vd_lo[vr][8 * pc]) = cat(l0, l1);
-        }
-        __syncthreads();
+        const int r = v_row < c ? v_row : c - 1;
+        __builtin_amdgcn_global_load_lds(vb + static_cast<uint32_t>(r) * row + 8 * v_unit,
+                                         (lds_void *)&sm.v[buf][16 * W * VB], 16, 0, 0);
+    };
 
-        if (ci + 1 < nchunks) {
-            const int64_t rem1 = rem - C;
-            fetch(t + C, static_cast<int>(rem1 < C ? rem1 : C));
+    // Decayed V of a staged chunk: thread tid converts V row tid/4, logical
+    // unit tid%4 (8 values) into hi/lo at the same (swizzled) position.
+    const int dv_row = tid >> 2;
+    const int dv_pos = v_off(dv_row, 8 * (tid & 3));
+    // weight of that row in a full chunk and in the last one (zero past its end)
+    const float vdec_full = expf(-lam * (static_cast<float>(C - 1 - dv_row) + vshift));
+    const float vdec_last = dv_row < c_last ? expf(-lam * (static_cast<float>(c_last - 1 - dv_row) + vshift)) : 0.f;
+    const float dc_full = expf(-lam * static_cast<float>(C));
+    const float dc_last = expf(-lam * static_cast<float>(c_last));
+    auto decay_v = [&](int buf, float vdec) {
+        const u16x8 pv = lds8(&sm.v[buf][dv_pos]);
+        f32x4 x0, x1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x0[e] = bf16_to_f32(pv[e]) * vdec;
+            x1[e] = bf16_to_f32(pv[4 + e]) * vdec;
         }
+        u16x4 h0, l0, h1, l1;
+        split4(x0, h0, l0);
+        split4(x1, h1, l1);
+        *reinterpret_cast<u16x8 *>(&sm.vd_hi[dv_pos]) = cat(h0, h1);
+        *reinterpret_cast<u16x8 *>(&sm.vd_lo[dv_pos]) = cat(l0, l1);
+    };
+
+    const uint32_t offo = 2u * (static_cast<uint32_t>(16 * W + l16) * row + 4 * g);
+
+    // Every call of issue_copies is 9 vector-memory instructions per wave.
+    // Before publishing chunk ci+1 a wave waits until only the copies of chunk
+    // ci+2 (issued later, in program order) may still be outstanding.
+    auto wait_all = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+    auto wait_all_but_one_chunk = [] { asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); };
+
+    // prologue: chunks 0 and 1 in flight, chunk 0 published and decayed
+    issue_copies(jb.t0, nchunks == 1 ? c_last : C, 0);
+    if (nchunks > 1) {
+        issue_copies(jb.t0 + C, nchunks == 2 ? c_last : C, 1);
+        wait_all_but_one_chunk();
+    } else {
+        wait_all();
+    }
+    __syncthreads();
+    decay_v(0, nchunks == 1 ? vdec_last : vdec_full);
+
+    int buf = 0;  // ring slot of chunk ci
+    for (int ci = 0; ci < nchunks; ++ci) {
+        const int64_t t = jb.t0 + static_cast<int64_t>(ci) * C;
+        const bool last = ci + 1 == nchunks;
+        const int c = last ? c_last : C;
+        const int nbuf = buf == NBUF - 1 ? 0 : buf + 1;       // slot of chunk ci+1
+        const int nnbuf = nbuf == NBUF - 1 ? 0 : nbuf + 1;    // slot of chunk ci+2
+        lds_barrier();  // chunk ci staged and decayed; previous partials consumed
+
+        const bool ahead = ci + 2 < nchunks;
+        if (ahead) issue_copies(t + 2 * C, ci + 3 == nchunks ? c_last : C, nnbuf);
 
         f32x4 part[4][2];
-        chunk_compute<W, kF>(sm, mdec, qdec, full ? dc_full : dc_last, g, l16, S, part);
+        if (!last)
+            chunk_compute<W, kF>(sm.q[buf], sm.k[buf], sm.v[buf], sm.vd_hi, sm.vd_lo, mdec, qdec, dc_full,
+                                 g, l16, S, part);
+        else
+            chunk_compute<W, kF>(sm.q[buf], sm.k[buf], sm.v[buf], sm.vd_hi, sm.vd_lo, mdec_last, qdec,
+                                 dc_last, g, l16, S, part);
 
         // hand the partial O^T tiles of the other row blocks to their owners
 #pragma unroll
@@ -407,12 +528,16 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
             if (it != W)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) sm.part[W][it][nt][lane] = part[it][nt];
-        __syncthreads();
+        if (ahead)
+            wait_all_but_one_chunk();  // this wave's copies of chunk ci+1 landed
+        else
+            wait_all();
+        lds_barrier();
 
         // row block W: sum the four partials and store o.
         // O^T tile nt, element r: value column col0 + 16nt + 4g + r, token 16W + l16
         char *ob = reinterpret_cast<char *>(jb.out + t * jb.row + jb.hcol + col0);
-        const bool store = full || (16 * W + l16) < c;
+        const bool store = !last || (16 * W + l16) < c;
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             f32x4 o = part[W][nt];
@@ -425,6 +550,10 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
                 *reinterpret_cast<uint64_t *>(ob + offo + 32 * nt) = packed;
             }
         }
+        // decayed V of the next chunk (its copies are visible after the barrier
+        // above, and this chunk's state update no longer reads vd)
+        if (!last) decay_v(nbuf, ci + 2 == nchunks ? vdec_last : vdec_full);
+        buf = nbuf;
     }
 
     const float unscale = kF ? expf(32.f * lam) : 1.f;
