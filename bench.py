@@ -19,8 +19,8 @@ Algorithmic traffic (bytes the method must move; bf16 I/O, fp32 state):
 Peaks: HBM 8 TB/s, bf16 dense MFMA 2.5 PFLOP/s.
 
 The CPU baseline runs the fp64 oracle on the host cores over a bounded sample
-of the prefill workload (a subset of heads, every token), scaled to tokens/s of
-the whole workload.
+of the prefill workload (four heads per core, at most all 64, every token),
+scaled to tokens/s of the whole workload.
 """
 from __future__ import annotations
 
@@ -37,8 +37,40 @@ D = 128
 STATE_BYTES = D * D * 4
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+KERNEL_SOURCES = {
+    "prefill_chunked_kernel": ["prefill_chunked.hip", "common.h"],
+    "recurrent_kernel<bf16>": ["recurrent.hip", "common.h"],
+}
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def source_sha256(kernel):
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "linear_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    counts (profiles/traffic.json), or None when they were taken on a different
+    version of the kernel's source or workload."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            entry = json.load(f).get(kernel, {}).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not entry or entry.get("source_sha256") != source_sha256(kernel):
+        return None
+    return entry.get("traffic_bytes")
 
 
 def prefill_bytes(T, H, B):
@@ -63,7 +95,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the oracle CPU baseline (for quick local runs)")
     ap.add_argument("--cpu-heads", type=int, default=0,
-                    help="heads in the CPU-baseline sample (default: one per host core, <= 64)")
+                    help="heads in the CPU-baseline sample (default: four per host core, <= 64)")
     ap.add_argument("--only", choices=["prefill", "decode", "verify"], default=None,
                     help="run one entry point only (profiling aid; the JSON line then "
                          "reports that call alone)")
@@ -205,7 +237,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": p_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": p_gbs / HBM_PEAK_GBS, "traffic": None,
+            "frac": p_gbs / HBM_PEAK_GBS,
+            "traffic": measured_traffic("prefill_chunked_kernel", "long-prefill"),
             "kernel": "prefill_chunked_kernel", "algorithmic_bytes": pb,
             "avg_ms": ms["prefill"],
             "mfma_useful_tflops": p_tflops, "mfma_useful_frac": p_tflops / BF16_PEAK_TFLOPS,
@@ -214,7 +247,8 @@ def main():
             "value": wd.batch / (ms["decode"] * 1e-3), "unit": "req/s", "avg_ms": ms["decode"],
             "min_ms": ms_min["decode"],
             "roofline": {"bound": "hbm", "achieved": d_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": d_gbs / HBM_PEAK_GBS, "traffic": None,
+                         "frac": d_gbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("recurrent_kernel<bf16>", "decode"),
                          "kernel": "recurrent_kernel<bf16>", "algorithmic_bytes": db},
         },
         "verify": {
@@ -222,7 +256,8 @@ def main():
             "tokens_per_s": wv.total_tokens / (ms["verify"] * 1e-3), "avg_ms": ms["verify"],
             "min_ms": ms_min["verify"],
             "roofline": {"bound": "hbm", "achieved": v_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": v_gbs / HBM_PEAK_GBS, "traffic": None,
+                         "frac": v_gbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("recurrent_kernel<bf16>", "verify"),
                          "kernel": "recurrent_kernel<bf16>", "algorithmic_bytes": vb},
         },
         "prefill_min_ms": ms_min["prefill"],
@@ -233,7 +268,7 @@ def main():
         import oracle
 
         cores = oracle.default_threads()
-        nh = args.cpu_heads or min(64, cores)
+        nh = args.cpu_heads or min(64, 4 * cores)
         heads = list(range(nh))
         slopes = oracle.alibi_slopes(H, wp.layer_id, wp.num_layers)[heads]
         q, k, v = (np.ascontiguousarray(x[:, heads]) for x in (wp.q, wp.k, wp.v))
