@@ -32,14 +32,32 @@ MUTANTS = {
     "decay_twice": ("exp(-jb->slopes[h])", "exp(-2.0 * jb->slopes[h])"),
     "dropped_prefix": ("memcpy(S, jb->init + ((size_t)b * H + h) * sdd, sdd * sizeof(double));",
                        "memset(S, 0, sdd * sizeof(double));"),
-    "dropped_last_token": ("t < jb->cu_seqlens[b + 1]; ++t", "t + 1 < jb->cu_seqlens[b + 1]; ++t"),
+    "dropped_last_token": ("t < t1; ++t", "t + 1 < t1; ++t"),
     "layer_factor_L": ("(double)layer_id / (double)(num_layers - 1)",
                        "(double)layer_id / (double)(num_layers)"),
     "layer_factor_no_eps": ("(double)(num_layers - 1) + 1e-5", "(double)(num_layers - 1)"),
     "alibi_odd_offset": ("(2 * j + 1)", "(2 * j + 2)"),
     "alibi_exponent": ("-8.0 * (double)(i + 1) / (double)m", "-8.0 * (double)(i) / (double)m"),
-    "wrong_head_stride": ("const double *kt = jb->k + ((size_t)t * H + h) * d;",
-                          "const double *kt = jb->k + ((size_t)t * H + (h ^ 1) % H) * d;"),
+    "wrong_head_stride": ("jb->k + ((size_t)t * HK + hk) * d", "jb->k + ((size_t)t * HK + (hk ^ 1) % HK) * d"),
+    "gqa_interleaved": ("const int hk = h / (H / HK); /* key/value head of query head h */",
+                        "const int hk = h % HK;"),
+    "track_one_late": ("if (snap && t - t0 == tl)", "if (snap && t - t0 == tl + 1)"),
+    "track_end_missing": ("if (snap && tl == t1 - t0)", "if (snap && tl == t1 - t0 && 0)"),
+    "tree_ignores_parent": ("const int p = jb->parents[(size_t)b * n + j];", "const int p = j - 1;"),
+    "tree_always_root": ("const double *from = p < 0 ?", "const double *from = 1 ?"),
+    "tree_parent_off_by_one": ("jb->draft_state + (((size_t)b * n + p) * H + h) * sdd",
+                               "jb->draft_state + (((size_t)b * n + (p > 0 ? p - 1 : p)) * H + h) * sdd"),
+    "tree_no_decay": ("""const int hk = h / (H / HK);
+    const double decay = exp(-jb->slopes[h]);
+    const double scale = 1.0 / sqrt((double)d);
+    const size_t sdd = (size_t)d * d;
+
+    for (int j = 0;""", """const int hk = h / (H / HK);
+    const double decay = 1.0;
+    const double scale = 1.0 / sqrt((double)d);
+    const size_t sdd = (size_t)d * d;
+
+    for (int j = 0;"""),
 }
 
 
@@ -52,21 +70,101 @@ def _build(tmp_path, name, text):
     lib = ctypes.CDLL(str(so))
     lib.la_oracle_run.restype = ctypes.c_int
     lib.la_oracle_alibi_slopes.restype = ctypes.c_int
+    lib.la_oracle_tree.restype = ctypes.c_int
     return lib
 
 
-def _run(lib, q, k, v, cu, S0, slopes):
+def _p(a):
+    return ctypes.c_void_p(a.ctypes.data) if a is not None else None
+
+
+def _run(lib, q, k, v, cu, S0, slopes, track=None):
     cu = np.ascontiguousarray(cu, dtype=np.int64)
     B = cu.shape[0] - 1
     H, d = S0.shape[1], S0.shape[2]
+    HK = k.shape[1]
     q, k, v, S0 = (np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v, S0))
     sl = np.ascontiguousarray(slopes, dtype=np.float64)
     out = np.zeros((int(cu[-1]), H, d))
     fin = np.zeros((B, H, d, d))
-    p = lambda a: ctypes.c_void_p(a.ctypes.data)
-    rc = lib.la_oracle_run(B, H, d, p(cu), p(q), p(k), p(v), p(S0), p(sl), p(out), p(fin), 2)
+    tl = None if track is None else np.ascontiguousarray(track, dtype=np.int64)
+    snap = None if track is None else np.full((B, H, d, d), np.nan)
+    rc = lib.la_oracle_run(B, H, HK, d, _p(cu), _p(q), _p(k), _p(v), _p(S0), _p(sl), _p(tl),
+                           _p(out), _p(fin), _p(snap), 2)
     assert rc == 0
-    return out, fin
+    return (out, fin) if track is None else (out, fin, snap)
+
+
+def _state_after(k, v, S0, lam, n):
+    w = np.exp(-lam * (n - 1 - np.arange(n)))
+    return math.exp(-lam * n) * S0 + np.einsum("s,si,sj->ij", w, k[:n], v[:n])
+
+
+def _gqa_ok(lib):
+    """Grouped heads: query head h against the closed form with kv head h // 2."""
+    rng = np.random.default_rng(4)
+    H, HK, d, T = 4, 2, 4, 6
+    q = rng.standard_normal((T, H, d))
+    k, v = rng.standard_normal((T, HK, d)), rng.standard_normal((T, HK, d))
+    S0 = 0.2 * rng.standard_normal((1, H, d, d))
+    lam = np.array([0.5, 0.2, 0.1, 0.02])
+    out, fin = _run(lib, q, k, v, [0, T], S0, lam)
+    for h in range(H):
+        S = _state_after(k[:, h // 2], v[:, h // 2], S0[0, h], lam[h], T)
+        if not np.allclose(fin[0, h], S, rtol=1e-10, atol=1e-12):
+            return False
+        if not np.allclose(out[T - 1, h], q[T - 1, h] @ S / math.sqrt(d), rtol=1e-10, atol=1e-12):
+            return False
+    return True
+
+
+def _track_ok(lib):
+    """Snapshots at 0, inside and at the end of a request against the closed form."""
+    rng = np.random.default_rng(5)
+    d, lens, tls = 4, [6, 6, 6], [0, 3, 6]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v = (rng.standard_normal((cu[-1], 1, d)) for _ in range(3))
+    S0 = 0.2 * rng.standard_normal((3, 1, d, d))
+    lam = 0.35
+    _, _, snap = _run(lib, q, k, v, cu, S0, np.array([lam]), track=tls)
+    for b in range(3):
+        sl = slice(cu[b], cu[b + 1])
+        if not np.allclose(snap[b, 0], _state_after(k[sl, 0], v[sl, 0], S0[b, 0], lam, tls[b]),
+                           rtol=1e-10, atol=1e-12):
+            return False
+    return True
+
+
+def _tree_ok(lib):
+    """A branching tree against the root-path closed form of every draft's state."""
+    rng = np.random.default_rng(6)
+    par = [-1, 0, 0, 2, -1, 4]
+    n, d = len(par), 4
+    q, k, v = (rng.standard_normal((n, 1, d)) for _ in range(3))
+    S0 = 0.2 * rng.standard_normal((1, 1, d, d))
+    lam = 0.3
+    out = np.zeros((n, 1, d))
+    st = np.zeros((1, n, 1, d, d))
+    pr = np.array(par, dtype=np.int32)
+    rc = lib.la_oracle_tree(1, n, 1, 1, d, _p(q), _p(k), _p(v), _p(S0), _p(np.array([lam])),
+                            _p(pr), _p(out), _p(st), 1)
+    if rc != 0:
+        return False
+    for j in range(n):
+        path, a = [], j
+        while a >= 0:
+            path.append(a)
+            a = par[a]
+        path = path[::-1]
+        m = len(path)
+        S = math.exp(-lam * m) * S0[0, 0]
+        for i, a in enumerate(path, start=1):
+            S = S + math.exp(-lam * (m - i)) * np.outer(k[a, 0], v[a, 0])
+        if not np.allclose(st[0, j, 0], S, rtol=1e-10, atol=1e-12):
+            return False
+        if not np.allclose(out[j, 0], q[j, 0] @ S / math.sqrt(d), rtol=1e-10, atol=1e-12):
+            return False
+    return True
 
 
 def _closed_form_ok(lib):
@@ -135,7 +233,8 @@ def _slopes_ok(lib):
     return True
 
 
-CHECKS = [_closed_form_ok, _cumsum_ok, _worked_example_ok, _slopes_ok]
+CHECKS = [_closed_form_ok, _cumsum_ok, _worked_example_ok, _slopes_ok, _gqa_ok, _track_ok,
+          _tree_ok]
 
 
 def test_unmodified_oracle_passes_checks(tmp_path):
