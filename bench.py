@@ -11,11 +11,20 @@ entry point's own rate is reported beside the step time.  `value` is the
 prefill rate in tokens/s; the decode rate (requests/s) and the verify rate
 are reported in their own objects, each with its roofline.
 
+After the timed steps, outside the step time:
+  * la_verify_tree  the verify batch (128 x 5 drafts, H=64) as a seeded random
+           draft tree per request, writing every per-position state
+  * graph  32 small decode calls (1 request, H=64, one pool per call, as one
+           per layer) launched eagerly and as one captured HIP graph: host
+           launch overhead per call, eager vs graph
+
 Algorithmic traffic (bytes the method must move; bf16 I/O, fp32 state):
   prefill: 1024 B per (token, head) for q, k, v in and o out, plus 128 KiB of
            state read + write per (request, head)
   decode / verify: 128 KiB of state read + write per (request, head) plus
            1 KiB of q, k, v, o per (token, head)
+  tree verify: 64 KiB state read per (request, head), 64 KiB state written
+           per (draft, head), 1 KiB of q, k, v, o per (draft, head)
 Peaks: HBM 8 TB/s, bf16 dense MFMA 2.5 PFLOP/s.
 
 The CPU baseline runs the fp64 oracle on the host cores over a bounded sample
@@ -87,6 +96,43 @@ def step_bytes(B, H, tokens):
     return B * H * 2 * STATE_BYTES + tokens * H * 4 * D * 2
 
 
+def tree_bytes(B, n, H):
+    return B * H * STATE_BYTES + B * n * H * STATE_BYTES + B * n * H * 4 * D * 2
+
+
+def graph_latency(la, W, np, torch, dev, upload, warmup, reps, layers=32, batch=1):
+    """Per-call time of `layers` small decode calls (one pool per call), launched
+    eagerly from Python and replayed as one captured HIP graph."""
+    wl = W.make("graph-decode", "decode", "bf16", 64, np.ones(batch, dtype=np.int64), batch,
+                seed=9, fill_all_slots=True)
+    g = upload(wl)
+    pools = [g["pool"].clone() for _ in range(layers)]
+    outs = [torch.empty_like(g["q"]) for _ in range(layers)]
+
+    def all_layers():
+        for l in range(layers):
+            la.la_decode(g["q"], g["k"], g["v"], pools[l], g["slot"], g["slopes"], outs[l])
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / (reps * layers)
+
+    eager_us = timed(all_layers)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        all_layers()
+    graph_us = timed(graph.replay)
+    return {"batch": batch, "num_heads": 64, "calls_per_graph": layers,
+            "eager_us_per_call": eager_us, "graph_us_per_call": graph_us,
+            "speedup": eager_us / graph_us}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -96,7 +142,7 @@ def main():
                     help="skip the oracle CPU baseline (for quick local runs)")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads in the CPU-baseline sample (default: four per host core, <= 64)")
-    ap.add_argument("--only", choices=["prefill", "decode", "verify"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "verify", "tree"], default=None,
                     help="run one entry point only (profiling aid; the JSON line then "
                          "reports that call alone)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -136,10 +182,10 @@ def main():
         return torch.from_numpy(x).view(torch.int16).view(torch.bfloat16).to(dev)
 
     t_gen = time.time()
-    want = {args.only} if args.only else {"prefill", "decode", "verify"}
+    want = {args.only} if args.only else {"prefill", "decode", "verify", "tree"}
     wp = W.config(4) if "prefill" in want else None
     wd = W.config(3) if "decode" in want else None
-    wv = W.config(5) if "verify" in want else None
+    wv = W.config(5) if want & {"verify", "tree"} else None
     log(f"inputs generated in {time.time() - t_gen:.1f} s")
 
     def upload(wl):
@@ -157,6 +203,16 @@ def main():
             X["out"] = torch.empty_like(X["q"])
     if V is not None:
         V["state_out"] = torch.empty((wv.batch, wv.num_heads, D, D), device=dev)
+    if "tree" in want:
+        # a seeded random draft tree per request: parent of draft j in [-1, j)
+        rng = np.random.default_rng(2024)
+        par = np.full((wv.batch, wv.num_draft), -1, dtype=np.int32)
+        for b in range(wv.batch):
+            for j in range(1, wv.num_draft):
+                par[b, j] = rng.integers(-1, j)
+        V["parents"] = torch.from_numpy(par).to(dev)
+        V["tree_out"] = torch.empty_like(V["q"])
+        V["draft_states"] = torch.empty((wv.batch, wv.num_draft, wv.num_heads, D, D), device=dev)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -173,10 +229,15 @@ def main():
         la.la_verify(V["q"], V["k"], V["v"], wv.num_draft, V["pool"], V["slot"], V["slopes"],
                      V["out"], V["state_out"], stream=stream)
 
+    def run_tree():
+        la.la_verify_tree(V["q"], V["k"], V["v"], wv.num_draft, V["pool"], V["slot"], V["parents"],
+                          V["slopes"], V["tree_out"], V["draft_states"], stream=stream)
+
     calls = [(n, f) for n, f in (("prefill", run_prefill), ("decode", run_decode),
                                  ("verify", run_verify)) if n in want]
+    extra = [("tree", run_tree)] if "tree" in want else []
     for _ in range(args.warmup):
-        for _, fn in calls:
+        for _, fn in calls + extra:
             fn()
     torch.cuda.synchronize()
 
@@ -193,9 +254,19 @@ def main():
             b.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms = {name: float(np.mean([a.elapsed_time(b) for a, b in ev[name]])) for name, _ in calls}
-    ms_min = {name: float(np.min([a.elapsed_time(b) for a, b in ev[name]])) for name, _ in calls}
     ms_per_step = elapsed * 1000.0 / K
+    # entry points outside the step: timed the same way, after it
+    for name, fn in extra:
+        ev[name] = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                    for _ in range(K)]
+        for s in range(K):
+            a, b = ev[name][s]
+            a.record(stream)
+            fn()
+            b.record(stream)
+    torch.cuda.synchronize()
+    ms = {name: float(np.mean([a.elapsed_time(b) for a, b in ev[name]])) for name in ev}
+    ms_min = {name: float(np.min([a.elapsed_time(b) for a, b in ev[name]])) for name in ev}
 
     if args.only:
         name = args.only
@@ -212,6 +283,9 @@ def main():
     vb = step_bytes(wv.batch, H, wv.total_tokens)
     d_gbs = db / (ms["decode"] * 1e-3) / 1e9
     v_gbs = vb / (ms["verify"] * 1e-3) / 1e9
+    tb = tree_bytes(wv.batch, wv.num_draft, H)
+    t_gbs = tb / (ms["tree"] * 1e-3) / 1e9
+    graph = graph_latency(la, W, np, torch, dev, upload, args.warmup, K)
 
     result = {
         "metric": METRIC,
@@ -260,6 +334,17 @@ def main():
                          "traffic": measured_traffic("recurrent_kernel<bf16>", "verify"),
                          "kernel": "recurrent_kernel<bf16>", "algorithmic_bytes": vb},
         },
+        "tree_verify": {
+            "value": wv.batch / (ms["tree"] * 1e-3), "unit": "req/s",
+            "tokens_per_s": wv.total_tokens / (ms["tree"] * 1e-3), "avg_ms": ms["tree"],
+            "min_ms": ms_min["tree"],
+            "config": {"batch": wv.batch, "num_draft": wv.num_draft, "num_heads": H,
+                       "tree": "seeded random parents in [-1, j)", "draft_states": True},
+            "roofline": {"bound": "hbm", "achieved": t_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": t_gbs / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "tree_kernel<bf16>", "algorithmic_bytes": tb},
+        },
+        "decode_graph": graph,
         "prefill_min_ms": ms_min["prefill"],
         "cpu_baseline": None,
     }

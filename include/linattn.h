@@ -19,18 +19,24 @@
  * §额外覆盖：mamba 状态跟踪与布局鲁棒性).
  *
  * Layouts (all row-major, contiguous, device memory owned by the caller):
- *   q, k, v, out   [T, H, d]  token-major, heads interleaved; identical memory
+ *   q, out         [T, H, d]  token-major, heads interleaved; identical memory
  *                  to the flattened [T, H*d] output ([LA-page] §生产环境不支持
  *                  item 4).  Element type given by `dtype`; out has the same
  *                  type as q (bf16 outputs are rounded to nearest even).
+ *   k, v           [T, Hkv, d], same element type.  Grouped heads: Hkv
+ *                  (num_kv_heads) divides H and query head h reads key/value
+ *                  head h / (H / Hkv); Hkv == H is plain multi-head.  The
+ *                  reference kernel asserts qo_heads == kv_heads ([LA-page]
+ *                  §输入与配置覆盖); here state and slope stay per query head
+ *                  and only k and v are shared within a group.
  *   state_pool     [pool_slots, H, d, d] float32.
  *   slot_idx       [batch] int32, distinct, in [0, pool_slots); any order.
  *   cu_seqlens     [batch+1] int32, cu_seqlens[0] = 0, non-decreasing,
  *                  cu_seqlens[batch] = total_tokens (packed varlen batch).
  *   slopes         [H] float32 per-head decay rates (see la_alibi_slopes).
- * q, k and v have the same head count H (no grouped heads, as in the
- * reference kernel's qo_heads == kv_heads assertion, [LA-page]
- * §输入与配置覆盖).  head_dim must be 128.
+ * head_dim (d) is 128 or 64 (the reference's kernels need at least 128 for
+ * decode and 64 for prefill, [LA-page] §输入与配置覆盖; both run here on
+ * every path).
  *
  * Calls are asynchronous on `stream` (0 = the null stream): the library does
  * no host synchronisation, no device-to-host reads and no allocation on these
@@ -61,7 +67,7 @@ typedef struct ihipStream_t *hipStream_t;
 typedef enum {
     LA_OK = 0,
     LA_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad metadata (LA_DEBUG) */
-    LA_ERR_UNSUPPORTED = -2, /* head_dim != 128, unknown dtype, num_draft <= 0 */
+    LA_ERR_UNSUPPORTED = -2, /* head_dim not 64/128, unknown dtype, num_draft <= 0 */
     LA_ERR_HIP = -3          /* a HIP runtime call or kernel launch failed */
 } la_status;
 
@@ -94,44 +100,77 @@ la_status la_alibi_slopes(int num_heads, int layer_id, int num_layers, float *sl
  * back in place; out receives every token's output.  A zero-length request is a
  * no-op.  max_seqlen is an upper bound on any request's length (0 means every
  * request is empty; the call then launches nothing).
- * bf16: chunked MFMA kernel (fp32 state, bf16 hi/lo operand splits).
- * fp32: token-recurrent fp32 kernel.
+ *
+ * State tracking ([LA-page] §额外覆盖：mamba 状态跟踪与布局鲁棒性):
+ * track_lens and track_slot_idx ([batch] int32 each, device) are both NULL
+ * (no tracking) or both given.  Request b with 0 <= track_slot_idx[b] <
+ * pool_slots and 0 <= track_lens[b] <= its length also writes its state after
+ * its first track_lens[b] tokens (the prefix state itself for 0) to
+ * state_pool[track_slot_idx[b]]; a negative track slot means no snapshot.
+ * Track slots must be distinct from each other and from every slot_idx entry.
+ *
+ * bf16, d = 128: chunked MFMA kernel (fp32 state, bf16 hi/lo operand splits).
+ * fp32, or d = 64: token-recurrent fp32 kernel.
  * Errors: LA_ERR_INVALID_ARG for NULL pointers (q/k/v/out may be NULL only when
- * total_tokens == 0), negative sizes, batch > pool_slots or, with LA_DEBUG=1,
- * inconsistent cu_seqlens/slot_idx; LA_ERR_UNSUPPORTED for head_dim != 128 or
- * an unknown dtype; LA_ERR_HIP on a launch failure.
+ * total_tokens == 0), negative sizes, num_kv_heads not dividing num_heads,
+ * only one of the two track arrays, batch > pool_slots or, with LA_DEBUG=1,
+ * inconsistent cu_seqlens/slot_idx/track arrays; LA_ERR_UNSUPPORTED for a
+ * head_dim other than 64/128 or an unknown dtype; LA_ERR_HIP on a launch
+ * failure.
  */
 la_status la_prefill(const void *q, const void *k, const void *v, la_dtype dtype,
                      const int32_t *cu_seqlens, int batch, int64_t total_tokens, int max_seqlen,
-                     int num_heads, int head_dim,
+                     int num_heads, int num_kv_heads, int head_dim,
                      float *state_pool, int64_t pool_slots, const int32_t *slot_idx,
+                     const int32_t *track_lens, const int32_t *track_slot_idx,
                      const float *slopes, void *out, hipStream_t stream);
 
 /*
- * Decode: one token per request (q, k, v, out are [batch, H, d]).  Each
- * request's state is read, advanced by one step of the recurrence and written
- * back in place ([LA-page] §输入与配置覆盖, the decode kernel's role).
- * Errors as for la_prefill (no cu_seqlens).
+ * Decode: one token per request (q, out are [batch, H, d]; k, v [batch, Hkv, d]).
+ * Each request's state is read, advanced by one step of the recurrence and
+ * written back in place ([LA-page] §输入与配置覆盖, the decode kernel's role).
+ * Errors as for la_prefill (no cu_seqlens or track arrays).
  */
 la_status la_decode(const void *q, const void *k, const void *v, la_dtype dtype,
-                    int batch, int num_heads, int head_dim,
+                    int batch, int num_heads, int num_kv_heads, int head_dim,
                     float *state_pool, int64_t pool_slots, const int32_t *slot_idx,
                     const float *slopes, void *out, hipStream_t stream);
 
 /*
  * Chain verify: request b owns the num_draft draft tokens
- * b*num_draft .. b*num_draft+num_draft-1 of q, k, v, out ([batch*num_draft, H, d])
- * and processes them as one chain from its pool state ([LA-page] §生产环境不支持
- * item 3: drafts are verified as a chain, topk = 1).  Outputs are written for
- * every draft token.  The final state goes to state_out[b] ([batch, H, d, d]
- * float32) and the pool is left untouched; with state_out == NULL the final
- * state is written back to the pool slot instead.
+ * b*num_draft .. b*num_draft+num_draft-1 of q, k, v, out and processes them as
+ * one chain from its pool state ([LA-page] §生产环境不支持 item 3: drafts are
+ * verified as a chain, topk = 1).  Outputs are written for every draft token.
+ * The final state goes to state_out[b] ([batch, H, d, d] float32) and the pool
+ * is left untouched; with state_out == NULL the final state is written back to
+ * the pool slot instead.
  * Errors as for la_decode, plus LA_ERR_UNSUPPORTED for num_draft <= 0.
  */
 la_status la_verify(const void *q, const void *k, const void *v, la_dtype dtype,
-                    int batch, int num_draft, int num_heads, int head_dim,
+                    int batch, int num_draft, int num_heads, int num_kv_heads, int head_dim,
                     float *state_pool, int64_t pool_slots, const int32_t *slot_idx,
                     const float *slopes, void *out, float *state_out, hipStream_t stream);
+
+/*
+ * Tree verify with per-position states ([LA-page] §生产环境不支持 item 3 and
+ * Next Work item 2: each draft token forks from its parent's saved state
+ * instead of continuing the chain).  Request b owns draft tokens
+ * b*num_draft .. b*num_draft+num_draft-1 of q, k, v, out.  parent_idx
+ * [batch, num_draft] int32 (device): parent_idx[b][j] is -1 (the request's
+ * pool state) or an earlier draft p < j.  Draft j's state is
+ *     S_j = exp(-slopes[h]) * S_parent + outer(k_j, v_j),   o_j = (q_j @ S_j) * d^-0.5.
+ * Parents (-1, 0, 1, ..., num_draft-2) are the chain of la_verify.
+ * draft_states [batch, num_draft, H, d, d] float32 receives every S_j (NULL:
+ * outputs only).  The pool is never written.
+ * A request whose slot or any parent is out of range gets zero outputs and no
+ * state written (with LA_DEBUG=1 the call returns LA_ERR_INVALID_ARG instead).
+ * Errors as for la_verify.
+ */
+la_status la_verify_tree(const void *q, const void *k, const void *v, la_dtype dtype,
+                         int batch, int num_draft, int num_heads, int num_kv_heads, int head_dim,
+                         const float *state_pool, int64_t pool_slots, const int32_t *slot_idx,
+                         const int32_t *parent_idx, const float *slopes, void *out,
+                         float *draft_states, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -24,7 +24,8 @@ LIB_PATH = os.path.join(_HERE, "liblinattn.so")
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, -1, -2, -3
 LA_DTYPE_BF16, LA_DTYPE_F32 = 0, 1
 
-EXPORTED = ("la_status_string", "la_alibi_slopes", "la_prefill", "la_decode", "la_verify")
+EXPORTED = ("la_status_string", "la_alibi_slopes", "la_prefill", "la_decode", "la_verify",
+            "la_verify_tree")
 
 _lib = None
 
@@ -50,12 +51,14 @@ def load():
     lib.la_status_string.restype = ctypes.c_char_p
     lib.la_alibi_slopes.argtypes = [I, I, I, P]
     lib.la_alibi_slopes.restype = I
-    lib.la_prefill.argtypes = [P, P, P, I, P, I, L, I, I, I, P, L, P, P, P, P]
+    lib.la_prefill.argtypes = [P, P, P, I, P, I, L, I, I, I, I, P, L, P, P, P, P, P, P]
     lib.la_prefill.restype = I
-    lib.la_decode.argtypes = [P, P, P, I, I, I, I, P, L, P, P, P, P]
+    lib.la_decode.argtypes = [P, P, P, I, I, I, I, I, P, L, P, P, P, P]
     lib.la_decode.restype = I
-    lib.la_verify.argtypes = [P, P, P, I, I, I, I, I, P, L, P, P, P, P, P]
+    lib.la_verify.argtypes = [P, P, P, I, I, I, I, I, I, P, L, P, P, P, P, P]
     lib.la_verify.restype = I
+    lib.la_verify_tree.argtypes = [P, P, P, I, I, I, I, I, I, P, L, P, P, P, P, P, P]
+    lib.la_verify_tree.restype = I
     _lib = lib
     return lib
 
@@ -114,70 +117,110 @@ def _shape(t):
     return tuple(t.shape)
 
 
-def la_prefill(q, k, v, cu_seqlens, state_pool, slot_idx, slopes, out, max_seqlen, stream=None):
-    """Packed varlen prefill.  q, k, v, out: [T, H, 128] bf16 or fp32;
-    cu_seqlens [B+1] int32; state_pool [P, H, 128, 128] fp32 (updated in place);
-    slot_idx [B] int32; slopes [H] fp32; max_seqlen: host int >= every length."""
+def _qkv_shapes(q, k, v, out, what):
+    """(N, H, Hkv, d) from q/out [N, H, d] and k/v [N, Hkv, d]; one dtype for all."""
+    N, H, d = _shape(q)
+    if _shape(out) != (N, H, d):
+        raise ValueError(f"out must have the shape of q [{what}, H, d]")
+    if k.dim() != 3 or k.shape[0] != N or k.shape[2] != d or _shape(v) != _shape(k):
+        raise ValueError(f"k and v must be [{what}, Hkv, d] with q's token count and head_dim")
+    if not (k.dtype == v.dtype == out.dtype == q.dtype):
+        raise TypeError("q, k, v, out must share one dtype")
+    return N, H, k.shape[1], d
+
+
+def la_prefill(q, k, v, cu_seqlens, state_pool, slot_idx, slopes, out, max_seqlen,
+               track_lens=None, track_slot_idx=None, stream=None):
+    """Packed varlen prefill.  q, out: [T, H, d]; k, v: [T, Hkv, d] (bf16 or fp32,
+    d = 64 or 128, Hkv dividing H); cu_seqlens [B+1] int32; state_pool
+    [P, H, d, d] fp32 (updated in place); slot_idx [B] int32; slopes [H] fp32;
+    max_seqlen: host int >= every length.  track_lens / track_slot_idx ([B] int32,
+    both or neither): snapshot of request b's state after track_lens[b] tokens
+    written to pool slot track_slot_idx[b] (negative: none)."""
     import torch
 
     io = (torch.bfloat16, torch.float32)
-    T, H, d = _shape(q)
-    if _shape(k) != (T, H, d) or _shape(v) != (T, H, d) or _shape(out) != (T, H, d):
-        raise ValueError("q, k, v, out must share the shape [T, H, d]")
-    if not (k.dtype == v.dtype == out.dtype == q.dtype):
-        raise TypeError("q, k, v, out must share one dtype")
+    T, H, HK, d = _qkv_shapes(q, k, v, out, "T")
     B = cu_seqlens.numel() - 1
     if slot_idx.numel() != B:
         raise ValueError("slot_idx must have one entry per request")
+    if (track_lens is None) != (track_slot_idx is None):
+        raise ValueError("track_lens and track_slot_idx go together")
+    if track_lens is not None and (track_lens.numel() != B or track_slot_idx.numel() != B):
+        raise ValueError("track arrays must have one entry per request")
+    i32 = (torch.int32,)
     rc = load().la_prefill(_ptr(q, "q", io), _ptr(k, "k", io), _ptr(v, "v", io), _io_dtype(q),
-                           _ptr(cu_seqlens, "cu_seqlens", (torch.int32,)), B, T, int(max_seqlen),
-                           H, d, _ptr(state_pool, "state_pool", (torch.float32,)),
-                           state_pool.shape[0], _ptr(slot_idx, "slot_idx", (torch.int32,), True),
+                           _ptr(cu_seqlens, "cu_seqlens", i32), B, T, int(max_seqlen), H, HK, d,
+                           _ptr(state_pool, "state_pool", (torch.float32,)), state_pool.shape[0],
+                           _ptr(slot_idx, "slot_idx", i32, True),
+                           _ptr(track_lens, "track_lens", i32, True),
+                           _ptr(track_slot_idx, "track_slot_idx", i32, True),
                            _ptr(slopes, "slopes", (torch.float32,)), _ptr(out, "out", io),
                            _stream(state_pool, stream))
     _check(rc, "la_prefill")
 
 
 def la_decode(q, k, v, state_pool, slot_idx, slopes, out, stream=None):
-    """One token per request: q, k, v, out [B, H, 128]; the pool is updated in place."""
+    """One token per request: q, out [B, H, d]; k, v [B, Hkv, d]; the pool is
+    updated in place."""
     import torch
 
     io = (torch.bfloat16, torch.float32)
-    B, H, d = _shape(q)
-    if _shape(k) != (B, H, d) or _shape(v) != (B, H, d) or _shape(out) != (B, H, d):
-        raise ValueError("q, k, v, out must share the shape [B, H, d]")
-    if not (k.dtype == v.dtype == out.dtype == q.dtype):
-        raise TypeError("q, k, v, out must share one dtype")
+    B, H, HK, d = _qkv_shapes(q, k, v, out, "B")
     if slot_idx.numel() != B:
         raise ValueError("slot_idx must have one entry per request")
     rc = load().la_decode(_ptr(q, "q", io), _ptr(k, "k", io), _ptr(v, "v", io), _io_dtype(q), B, H,
-                          d, _ptr(state_pool, "state_pool", (torch.float32,)), state_pool.shape[0],
-                          _ptr(slot_idx, "slot_idx", (torch.int32,), True),
+                          HK, d, _ptr(state_pool, "state_pool", (torch.float32,)),
+                          state_pool.shape[0], _ptr(slot_idx, "slot_idx", (torch.int32,), True),
                           _ptr(slopes, "slopes", (torch.float32,)), _ptr(out, "out", io),
                           _stream(state_pool, stream))
     _check(rc, "la_decode")
 
 
 def la_verify(q, k, v, num_draft, state_pool, slot_idx, slopes, out, state_out=None, stream=None):
-    """Chain verify: q, k, v, out [B*num_draft, H, 128]; the final states go to
-    state_out [B, H, 128, 128] (pool untouched) or, if None, back to the pool."""
+    """Chain verify: q, out [B*num_draft, H, d]; k, v [B*num_draft, Hkv, d]; the
+    final states go to state_out [B, H, d, d] (pool untouched) or, if None,
+    back to the pool."""
     import torch
 
     io = (torch.bfloat16, torch.float32)
-    N, H, d = _shape(q)
+    N, H, HK, d = _qkv_shapes(q, k, v, out, "B*num_draft")
     B = slot_idx.numel()
     if N != B * int(num_draft):
         raise ValueError("q must hold num_draft tokens per request")
-    if _shape(k) != (N, H, d) or _shape(v) != (N, H, d) or _shape(out) != (N, H, d):
-        raise ValueError("q, k, v, out must share one shape")
-    if not (k.dtype == v.dtype == out.dtype == q.dtype):
-        raise TypeError("q, k, v, out must share one dtype")
     if state_out is not None and _shape(state_out) != (B, H, d, d):
         raise ValueError("state_out must be [B, H, d, d]")
     rc = load().la_verify(_ptr(q, "q", io), _ptr(k, "k", io), _ptr(v, "v", io), _io_dtype(q), B,
-                          int(num_draft), H, d, _ptr(state_pool, "state_pool", (torch.float32,)),
+                          int(num_draft), H, HK, d, _ptr(state_pool, "state_pool", (torch.float32,)),
                           state_pool.shape[0], _ptr(slot_idx, "slot_idx", (torch.int32,), True),
                           _ptr(slopes, "slopes", (torch.float32,)), _ptr(out, "out", io),
                           _ptr(state_out, "state_out", (torch.float32,), True),
                           _stream(state_pool, stream))
     _check(rc, "la_verify")
+
+
+def la_verify_tree(q, k, v, num_draft, state_pool, slot_idx, parent_idx, slopes, out,
+                   draft_states=None, stream=None):
+    """Tree verify: q, out [B*n, H, d]; k, v [B*n, Hkv, d]; parent_idx [B, n] int32
+    with parent_idx[b][j] in [-1, j) (-1: the pool state); draft_states
+    [B, n, H, d, d] fp32 receives the state after every draft (None: outputs only).
+    The pool is not written."""
+    import torch
+
+    io = (torch.bfloat16, torch.float32)
+    N, H, HK, d = _qkv_shapes(q, k, v, out, "B*num_draft")
+    B, n = slot_idx.numel(), int(num_draft)
+    if N != B * n:
+        raise ValueError("q must hold num_draft tokens per request")
+    if parent_idx.numel() != B * n:
+        raise ValueError("parent_idx must be [B, num_draft]")
+    if draft_states is not None and _shape(draft_states) != (B, n, H, d, d):
+        raise ValueError("draft_states must be [B, num_draft, H, d, d]")
+    rc = load().la_verify_tree(_ptr(q, "q", io), _ptr(k, "k", io), _ptr(v, "v", io), _io_dtype(q),
+                               B, n, H, HK, d, _ptr(state_pool, "state_pool", (torch.float32,)),
+                               state_pool.shape[0], _ptr(slot_idx, "slot_idx", (torch.int32,), True),
+                               _ptr(parent_idx, "parent_idx", (torch.int32,), True),
+                               _ptr(slopes, "slopes", (torch.float32,)), _ptr(out, "out", io),
+                               _ptr(draft_states, "draft_states", (torch.float32,), True),
+                               _stream(state_pool, stream))
+    _check(rc, "la_verify_tree")

@@ -10,38 +10,43 @@
 #include <cstring>
 #include <vector>
 
+#include "common.h"
 #include "launch.h"
 #include "linattn.h"
 
 namespace {
 
 constexpr int64_t kMaxGrid = 0x7fffffff;
-constexpr int kSupportedHeadDim = 128;  // the kernels are written for d = 128
 
 bool debug_mode() {
     const char *s = std::getenv("LA_DEBUG");
     return s && s[0] == '1';
 }
 
+template <typename T>
+bool copy_to_host(std::vector<T> &dst, const T *src, size_t n) {
+    dst.resize(n > 0 ? n : 1);
+    return n == 0 || hipMemcpy(dst.data(), src, sizeof(T) * n, hipMemcpyDeviceToHost) == hipSuccess;
+}
+
 // Debug-mode validation of device-resident metadata ([LA-page] §生产环境不支持
 // item 1: unsupported inputs are rejected before the kernel runs).  Synchronises
-// `stream`.  cu_seqlens may be null (fixed-length requests).
+// `stream`.  cu_seqlens may be null (fixed-length requests of `fixed_len`
+// tokens); track arrays and parents may be null.
 la_status debug_check(const int32_t *cu_seqlens, int batch, int64_t total_tokens, int max_seqlen,
-                      const int32_t *slot_idx, int64_t pool_slots, hipStream_t stream) {
-    std::vector<int32_t> slots(batch > 0 ? batch : 1);
-    std::vector<int32_t> cu(batch + 1);
+                      int fixed_len, const int32_t *slot_idx, int64_t pool_slots,
+                      const int32_t *track_lens, const int32_t *track_slot_idx,
+                      const int32_t *parents, hipStream_t stream) {
+    std::vector<int32_t> slots, cu, tl, ts, par;
     if (hipStreamSynchronize(stream) != hipSuccess) return LA_ERR_HIP;
-    if (batch > 0 &&
-        hipMemcpy(slots.data(), slot_idx, sizeof(int32_t) * batch, hipMemcpyDeviceToHost) != hipSuccess)
-        return LA_ERR_HIP;
+    if (!copy_to_host(slots, slot_idx, batch)) return LA_ERR_HIP;
+    std::vector<int64_t> lens(batch > 0 ? batch : 1, fixed_len);
     if (cu_seqlens) {
-        if (hipMemcpy(cu.data(), cu_seqlens, sizeof(int32_t) * (batch + 1), hipMemcpyDeviceToHost) !=
-            hipSuccess)
-            return LA_ERR_HIP;
+        if (!copy_to_host(cu, cu_seqlens, batch + 1)) return LA_ERR_HIP;
         if (cu[0] != 0 || cu[batch] != total_tokens) return LA_ERR_INVALID_ARG;
         for (int b = 0; b < batch; ++b) {
-            const int64_t n = static_cast<int64_t>(cu[b + 1]) - cu[b];
-            if (n < 0 || n > max_seqlen) return LA_ERR_INVALID_ARG;
+            lens[b] = static_cast<int64_t>(cu[b + 1]) - cu[b];
+            if (lens[b] < 0 || lens[b] > max_seqlen) return LA_ERR_INVALID_ARG;
         }
     }
     std::vector<char> seen(static_cast<size_t>(pool_slots), 0);
@@ -50,17 +55,36 @@ la_status debug_check(const int32_t *cu_seqlens, int batch, int64_t total_tokens
         if (s < 0 || s >= pool_slots || seen[s]) return LA_ERR_INVALID_ARG;
         seen[s] = 1;
     }
+    if (track_lens) {
+        if (!copy_to_host(tl, track_lens, batch) || !copy_to_host(ts, track_slot_idx, batch))
+            return LA_ERR_HIP;
+        for (int b = 0; b < batch; ++b) {
+            if (ts[b] < 0) continue;  // no snapshot for this request
+            if (ts[b] >= pool_slots || seen[ts[b]] || tl[b] < 0 || tl[b] > lens[b])
+                return LA_ERR_INVALID_ARG;
+            seen[ts[b]] = 1;
+        }
+    }
+    if (parents) {
+        if (!copy_to_host(par, parents, static_cast<size_t>(batch) * fixed_len)) return LA_ERR_HIP;
+        for (size_t i = 0; i < static_cast<size_t>(batch) * fixed_len; ++i) {
+            const int j = static_cast<int>(i % fixed_len);
+            if (par[i] < -1 || par[i] >= j) return LA_ERR_INVALID_ARG;
+        }
+    }
     return LA_OK;
 }
 
 la_status common_checks(const void *q, const void *k, const void *v, la_dtype dtype,
-                        int64_t total_tokens, int batch, int num_heads, int head_dim,
-                        const float *state_pool, int64_t pool_slots, const int32_t *slot_idx,
-                        const float *slopes, const void *out) {
-    if (batch < 0 || num_heads <= 0 || head_dim <= 0 || pool_slots <= 0 || total_tokens < 0)
+                        int64_t total_tokens, int batch, int num_heads, int num_kv_heads,
+                        int head_dim, const float *state_pool, int64_t pool_slots,
+                        const int32_t *slot_idx, const float *slopes, const void *out) {
+    if (batch < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || pool_slots <= 0 ||
+        total_tokens < 0)
         return LA_ERR_INVALID_ARG;
+    if (num_heads % num_kv_heads != 0) return LA_ERR_INVALID_ARG;
     if (dtype != LA_DTYPE_BF16 && dtype != LA_DTYPE_F32) return LA_ERR_UNSUPPORTED;
-    if (head_dim != kSupportedHeadDim) return LA_ERR_UNSUPPORTED;
+    if (head_dim != 128 && head_dim != 64) return LA_ERR_UNSUPPORTED;
     if (batch > pool_slots) return LA_ERR_INVALID_ARG;  // slots must be distinct
     if (!state_pool || !slopes || (batch > 0 && !slot_idx)) return LA_ERR_INVALID_ARG;
     if (total_tokens > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
@@ -104,58 +128,129 @@ la_status la_alibi_slopes(int num_heads, int layer_id, int num_layers, float *sl
 
 la_status la_prefill(const void *q, const void *k, const void *v, la_dtype dtype,
                      const int32_t *cu_seqlens, int batch, int64_t total_tokens, int max_seqlen,
-                     int num_heads, int head_dim, float *state_pool, int64_t pool_slots,
-                     const int32_t *slot_idx, const float *slopes, void *out, hipStream_t stream) {
-    la_status st = common_checks(q, k, v, dtype, total_tokens, batch, num_heads, head_dim,
-                                 state_pool, pool_slots, slot_idx, slopes, out);
+                     int num_heads, int num_kv_heads, int head_dim, float *state_pool,
+                     int64_t pool_slots, const int32_t *slot_idx, const int32_t *track_lens,
+                     const int32_t *track_slot_idx, const float *slopes, void *out,
+                     hipStream_t stream) {
+    la_status st = common_checks(q, k, v, dtype, total_tokens, batch, num_heads, num_kv_heads,
+                                 head_dim, state_pool, pool_slots, slot_idx, slopes, out);
     if (st != LA_OK) return st;
     if (max_seqlen < 0 || (batch > 0 && !cu_seqlens)) return LA_ERR_INVALID_ARG;
+    if (!track_lens != !track_slot_idx) return LA_ERR_INVALID_ARG;
     if (debug_mode()) {
-        st = debug_check(cu_seqlens, batch, total_tokens, max_seqlen, slot_idx, pool_slots, stream);
+        st = debug_check(cu_seqlens, batch, total_tokens, max_seqlen, 0, slot_idx, pool_slots,
+                         track_lens, track_slot_idx, nullptr, stream);
         if (st != LA_OK) return st;
     }
-    if (batch == 0 || max_seqlen == 0 || total_tokens == 0) return LA_OK;
-    if (dtype == LA_DTYPE_BF16)
-        return from_hip(la::launch_prefill_chunked(
-            static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
-            static_cast<const uint16_t *>(v), cu_seqlens, batch, num_heads, total_tokens,
-            state_pool, pool_slots, slot_idx, slopes, static_cast<uint16_t *>(out), stream));
-    return from_hip(la::launch_recurrent(false, q, k, v, cu_seqlens, 0, batch, num_heads,
-                                         total_tokens, state_pool, pool_slots, slot_idx, slopes,
-                                         out, nullptr, stream));
+    // with every request empty there is nothing to compute, but a snapshot
+    // after 0 tokens still copies the prefix state
+    if (batch == 0 || ((max_seqlen == 0 || total_tokens == 0) && !track_lens)) return LA_OK;
+    if (dtype == LA_DTYPE_BF16 && head_dim == la::kHeadDim) {
+        la::PrefillArgs a{};
+        a.q = static_cast<const uint16_t *>(q);
+        a.k = static_cast<const uint16_t *>(k);
+        a.v = static_cast<const uint16_t *>(v);
+        a.cu_seqlens = cu_seqlens;
+        a.num_heads = num_heads;
+        a.num_kv_heads = num_kv_heads;
+        a.total_tokens = total_tokens;
+        a.pool = state_pool;
+        a.pool_slots = pool_slots;
+        a.slot_idx = slot_idx;
+        a.track_lens = track_lens;
+        a.track_slot_idx = track_slot_idx;
+        a.slopes = slopes;
+        a.out = static_cast<uint16_t *>(out);
+        return from_hip(la::launch_prefill_chunked(a, batch, stream));
+    }
+    la::RecurrentArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.cu_seqlens = cu_seqlens;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.total_tokens = total_tokens;
+    a.pool = state_pool;
+    a.pool_slots = pool_slots;
+    a.slot_idx = slot_idx;
+    a.track_lens = track_lens;
+    a.track_slot_idx = track_slot_idx;
+    a.slopes = slopes;
+    a.out = out;
+    return from_hip(la::launch_recurrent(a, dtype == LA_DTYPE_BF16, head_dim, batch, stream));
 }
 
 la_status la_decode(const void *q, const void *k, const void *v, la_dtype dtype, int batch,
-                    int num_heads, int head_dim, float *state_pool, int64_t pool_slots,
-                    const int32_t *slot_idx, const float *slopes, void *out, hipStream_t stream) {
-    la_status st = common_checks(q, k, v, dtype, batch, batch, num_heads, head_dim, state_pool,
-                                 pool_slots, slot_idx, slopes, out);
-    if (st != LA_OK) return st;
-    if (debug_mode()) {
-        st = debug_check(nullptr, batch, batch, 1, slot_idx, pool_slots, stream);
-        if (st != LA_OK) return st;
-    }
-    return from_hip(la::launch_recurrent(dtype == LA_DTYPE_BF16, q, k, v, nullptr, 1, batch,
-                                         num_heads, batch, state_pool, pool_slots, slot_idx,
-                                         slopes, out, nullptr, stream));
+                    int num_heads, int num_kv_heads, int head_dim, float *state_pool,
+                    int64_t pool_slots, const int32_t *slot_idx, const float *slopes, void *out,
+                    hipStream_t stream) {
+    return la_verify(q, k, v, dtype, batch, 1, num_heads, num_kv_heads, head_dim, state_pool,
+                     pool_slots, slot_idx, slopes, out, nullptr, stream);
 }
 
 la_status la_verify(const void *q, const void *k, const void *v, la_dtype dtype, int batch,
-                    int num_draft, int num_heads, int head_dim, float *state_pool,
-                    int64_t pool_slots, const int32_t *slot_idx, const float *slopes, void *out,
-                    float *state_out, hipStream_t stream) {
+                    int num_draft, int num_heads, int num_kv_heads, int head_dim,
+                    float *state_pool, int64_t pool_slots, const int32_t *slot_idx,
+                    const float *slopes, void *out, float *state_out, hipStream_t stream) {
     if (num_draft <= 0) return batch < 0 ? LA_ERR_INVALID_ARG : LA_ERR_UNSUPPORTED;
     const int64_t tokens = static_cast<int64_t>(batch) * num_draft;
-    la_status st = common_checks(q, k, v, dtype, tokens, batch, num_heads, head_dim, state_pool,
-                                 pool_slots, slot_idx, slopes, out);
+    la_status st = common_checks(q, k, v, dtype, tokens, batch, num_heads, num_kv_heads, head_dim,
+                                 state_pool, pool_slots, slot_idx, slopes, out);
     if (st != LA_OK) return st;
     if (debug_mode()) {
-        st = debug_check(nullptr, batch, tokens, num_draft, slot_idx, pool_slots, stream);
+        st = debug_check(nullptr, batch, tokens, num_draft, num_draft, slot_idx, pool_slots,
+                         nullptr, nullptr, nullptr, stream);
         if (st != LA_OK) return st;
     }
-    return from_hip(la::launch_recurrent(dtype == LA_DTYPE_BF16, q, k, v, nullptr, num_draft,
-                                         batch, num_heads, tokens, state_pool, pool_slots,
-                                         slot_idx, slopes, out, state_out, stream));
+    la::RecurrentArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.tokens_per_req = num_draft;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.total_tokens = tokens;
+    a.pool = state_pool;
+    a.pool_slots = pool_slots;
+    a.slot_idx = slot_idx;
+    a.slopes = slopes;
+    a.out = out;
+    a.state_out = state_out;
+    return from_hip(la::launch_recurrent(a, dtype == LA_DTYPE_BF16, head_dim, batch, stream));
+}
+
+la_status la_verify_tree(const void *q, const void *k, const void *v, la_dtype dtype, int batch,
+                         int num_draft, int num_heads, int num_kv_heads, int head_dim,
+                         const float *state_pool, int64_t pool_slots, const int32_t *slot_idx,
+                         const int32_t *parent_idx, const float *slopes, void *out,
+                         float *draft_states, hipStream_t stream) {
+    if (num_draft <= 0) return batch < 0 ? LA_ERR_INVALID_ARG : LA_ERR_UNSUPPORTED;
+    const int64_t tokens = static_cast<int64_t>(batch) * num_draft;
+    la_status st = common_checks(q, k, v, dtype, tokens, batch, num_heads, num_kv_heads, head_dim,
+                                 state_pool, pool_slots, slot_idx, slopes, out);
+    if (st != LA_OK) return st;
+    if (batch > 0 && !parent_idx) return LA_ERR_INVALID_ARG;
+    if (debug_mode()) {
+        st = debug_check(nullptr, batch, tokens, num_draft, num_draft, slot_idx, pool_slots,
+                         nullptr, nullptr, parent_idx, stream);
+        if (st != LA_OK) return st;
+    }
+    la::TreeArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.num_draft = num_draft;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.pool = state_pool;
+    a.pool_slots = pool_slots;
+    a.slot_idx = slot_idx;
+    a.parent_idx = parent_idx;
+    a.slopes = slopes;
+    a.out = out;
+    a.draft_states = draft_states;
+    return from_hip(la::launch_tree(a, dtype == LA_DTYPE_BF16, head_dim, batch, stream));
 }
 
 }  // extern "C"

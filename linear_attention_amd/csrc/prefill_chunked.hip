@@ -44,6 +44,12 @@
 // 16-byte units so that every read pattern here is free of bank conflicts.
 // Rows past the end of a short last chunk are loaded from the chunk's last
 // row (always in bounds) and given zero weight.
+//
+// State tracking ([LA-page] §额外覆盖): a request that snapshots its state
+// after tl tokens runs as two consecutive passes, over [0, tl) and [tl, len);
+// the first pass stores its final state to the track slot and the second
+// starts from it.  Grouped heads read k and v at the query head's group
+// (head h / (H / Hkv)) with their own token stride.
 #include "common.h"
 #include "launch.h"
 
@@ -386,9 +392,11 @@ __device__ __forceinline__ void lds_barrier() {
 struct Job {
     const uint16_t *q, *k, *v;
     uint16_t *out;
-    float *state;   // this (request, head)'s pool slot
-    int64_t t0, len;
-    size_t row, hcol;
+    const float *state_in;  // state before the pass
+    float *state_out;       // state after the pass
+    int64_t t0, len;        // tokens [t0, t0 + len), len >= 1
+    size_t row, hcol;       // q/out token stride and head column
+    size_t kvrow, kvcol;    // k/v token stride and head column
     int col0;
     float lam;
 };
@@ -428,7 +436,7 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                S[mt][nt][r] = sigma * jb.state[(32 * W + 16 * mt + 4 * g + r) * D + col0 + 16 * nt + l16];
+                S[mt][nt][r] = sigma * jb.state_in[(32 * W + 16 * mt + 4 * g + r) * D + col0 + 16 * nt + l16];
 
     // Async staging.  Wave W copies Q/K rows 16W..16W+15 (4 instructions of
     // 4 rows each) and V rows 16W..16W+15 (one instruction); lane L of a copy
@@ -442,21 +450,23 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
     }
     const int v_row = 16 * W + (lane >> 2);
     const int v_unit = (lane & 3) ^ swv(v_row);
+    const uint32_t kvrow = static_cast<uint32_t>(jb.kvrow);
     auto issue_copies = [&](int64_t t, int c, int buf) {
         const uint16_t *qb = jb.q + t * jb.row + jb.hcol;
-        const uint16_t *kb = jb.k + t * jb.row + jb.hcol;
-        const uint16_t *vb = jb.v + t * jb.row + jb.hcol + col0;
+        const uint16_t *kb = jb.k + t * jb.kvrow + jb.kvcol;
+        const uint16_t *vb = jb.v + t * jb.kvrow + jb.kvcol + col0;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int r = qk_row[u] < c ? qk_row[u] : c - 1;
-            const uint32_t off = static_cast<uint32_t>(r) * row + 8 * qk_unit[u];
+            const uint32_t r = static_cast<uint32_t>(qk_row[u] < c ? qk_row[u] : c - 1);
             const int dst = (16 * W + 4 * u) * D;
-            __builtin_amdgcn_global_load_lds(qb + off, (lds_void *)&sm.q[buf][dst], 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(kb + off, (lds_void *)&sm.k[buf][dst], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(qb + (r * row + 8 * qk_unit[u]), (lds_void *)&sm.q[buf][dst], 16,
+                                             0, 0);
+            __builtin_amdgcn_global_load_lds(kb + (r * kvrow + 8 * qk_unit[u]), (lds_void *)&sm.k[buf][dst],
+                                             16, 0, 0);
         }
-        const int r = v_row < c ? v_row : c - 1;
-        __builtin_amdgcn_global_load_lds(vb + static_cast<uint32_t>(r) * row + 8 * v_unit,
-                                         (lds_void *)&sm.v[buf][16 * W * VB], 16, 0, 0);
+        const uint32_t r = static_cast<uint32_t>(v_row < c ? v_row : c - 1);
+        __builtin_amdgcn_global_load_lds(vb + (r * kvrow + 8 * v_unit), (lds_void *)&sm.v[buf][16 * W * VB], 16,
+                                         0, 0);
     };
 
     // Decayed V of a staged chunk: thread tid converts V row tid/4, logical
@@ -563,71 +573,111 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                jb.state[(32 * W + 16 * mt + 4 * g + r) * D + col0 + 16 * nt + l16] = S[mt][nt][r] * unscale;
+                jb.state_out[(32 * W + 16 * mt + 4 * g + r) * D + col0 + 16 * nt + l16] = S[mt][nt][r] * unscale;
 }
 
-__global__ __launch_bounds__(NT) void prefill_chunked_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k, const uint16_t *__restrict__ v,
-    const int32_t *__restrict__ cu_seqlens, int num_heads, int pairs, int64_t total_tokens,
-    float *__restrict__ pool, int64_t pool_slots, const int32_t *__restrict__ slot_idx,
-    const float *__restrict__ slopes, uint16_t *__restrict__ out) {
+// The passes of wave W over a request: one over [0, len), or with a snapshot
+// inside the request [0, tl) into the track slot and then [tl, len) from it.
+template <int W, bool kF>
+__device__ __forceinline__ void run_passes(Smem &sm, const Job &base, float *track, int64_t tl) {
+    if (!track) {
+        run_wave<W, kF>(sm, base);
+        return;
+    }
+    for (int i = 0; i < 2; ++i) {
+        Job jb = base;
+        jb.t0 = i == 0 ? base.t0 : base.t0 + tl;
+        jb.len = i == 0 ? tl : base.len - tl;
+        jb.state_in = i == 0 ? base.state_in : track;
+        jb.state_out = i == 0 ? track : base.state_out;
+        run_wave<W, kF>(sm, jb);
+    }
+}
+
+__global__ __launch_bounds__(NT) void prefill_chunked_kernel(PrefillArgs a) {
     __shared__ Smem sm;
 
+    const int H = a.num_heads;
     int pair, vb;
-    map_block(blockIdx.x, pairs, pair, vb);
-    const int b = pair / num_heads;
-    const int h = pair - b * num_heads;
+    map_block(blockIdx.x, a.pairs, pair, vb);
+    const int b = pair / H;
+    const int h = pair - b * H;
     const int tid = threadIdx.x;
 
-    int64_t t0 = cu_seqlens[b], t1 = cu_seqlens[b + 1];
-    t0 = t0 < 0 ? 0 : (t0 > total_tokens ? total_tokens : t0);
-    t1 = t1 < t0 ? t0 : (t1 > total_tokens ? total_tokens : t1);
+    int64_t t0 = a.cu_seqlens[b], t1 = a.cu_seqlens[b + 1];
+    t0 = t0 < 0 ? 0 : (t0 > a.total_tokens ? a.total_tokens : t0);
+    t1 = t1 < t0 ? t0 : (t1 > a.total_tokens ? a.total_tokens : t1);
     const int64_t len = t1 - t0;
-    if (len <= 0) return;  // empty request: no-op
 
-    const size_t row = static_cast<size_t>(num_heads) * D;
+    const size_t row = static_cast<size_t>(H) * D;
     const size_t hcol = static_cast<size_t>(h) * D;
     const int col0 = vb * VB;
-    const int slot = slot_idx[b];
-    if (slot < 0 || slot >= pool_slots) {
+    const int slot = a.slot_idx[b];
+    if (slot < 0 || slot >= a.pool_slots) {
         // out-of-range slot: zero output for this column block, no state touched
         for (int64_t idx = tid; idx < len * (VB / 8); idx += NT) {
             const int64_t t = t0 + idx / (VB / 8);
-            *reinterpret_cast<u16x8 *>(out + t * row + hcol + col0 + 8 * (idx % (VB / 8))) =
+            *reinterpret_cast<u16x8 *>(a.out + t * row + hcol + col0 + 8 * (idx % (VB / 8))) =
                 u16x8{0, 0, 0, 0, 0, 0, 0, 0};
         }
         return;
     }
-    Job jb{q, k, v, out, pool + (static_cast<size_t>(slot) * num_heads + h) * (D * D), t0, len,
-           row, hcol, col0, slopes[h]};
+    float *state = a.pool + (static_cast<size_t>(slot) * H + h) * (D * D);
+    float *track = nullptr;
+    int64_t tl = len;
+    if (a.track_lens) {
+        const int ts = a.track_slot_idx[b];
+        const int64_t n = a.track_lens[b];
+        if (ts >= 0 && ts < a.pool_slots && n >= 0 && n <= len) {
+            track = a.pool + (static_cast<size_t>(ts) * H + h) * (D * D);
+            tl = n;
+        }
+    }
+    if (track && (tl == 0 || len == 0)) {
+        // snapshot after 0 tokens: a copy of this block's prefix state
+        for (int e = tid; e < D * VB; e += NT) {
+            const int r = e / VB, c = col0 + e % VB;
+            track[r * D + c] = state[r * D + c];
+        }
+    }
+    if (len <= 0) return;  // empty request: no-op
+    const int hk = h / (H / a.num_kv_heads);
+    const Job base{a.q, a.k, a.v, a.out, state, state, t0, len, row, hcol,
+                   static_cast<size_t>(a.num_kv_heads) * D, static_cast<size_t>(hk) * D, col0, a.slopes[h]};
+    // a snapshot strictly inside the request splits it into two passes
+    float *split = track && tl > 0 && tl < len ? track : nullptr;
     // slopes in [0, 2] take the factored decay path (the largest ALiBi slope
     // is below 1); anything else the explicit one
-    const bool factored = jb.lam >= 0.f && jb.lam <= 2.f;
+    const bool factored = base.lam >= 0.f && base.lam <= 2.f;
     switch (__builtin_amdgcn_readfirstlane(tid >> 6) + (factored ? 0 : 4)) {
-    case 0: run_wave<0, true>(sm, jb); break;
-    case 1: run_wave<1, true>(sm, jb); break;
-    case 2: run_wave<2, true>(sm, jb); break;
-    case 3: run_wave<3, true>(sm, jb); break;
-    case 4: run_wave<0, false>(sm, jb); break;
-    case 5: run_wave<1, false>(sm, jb); break;
-    case 6: run_wave<2, false>(sm, jb); break;
-    default: run_wave<3, false>(sm, jb); break;
+    case 0: run_passes<0, true>(sm, base, split, tl); break;
+    case 1: run_passes<1, true>(sm, base, split, tl); break;
+    case 2: run_passes<2, true>(sm, base, split, tl); break;
+    case 3: run_passes<3, true>(sm, base, split, tl); break;
+    case 4: run_passes<0, false>(sm, base, split, tl); break;
+    case 5: run_passes<1, false>(sm, base, split, tl); break;
+    case 6: run_passes<2, false>(sm, base, split, tl); break;
+    default: run_passes<3, false>(sm, base, split, tl); break;
+    }
+    if (track && tl == len) {
+        // snapshot after the whole request: the final state, as stored above
+        __syncthreads();
+        for (int e = tid; e < D * VB; e += NT) {
+            const int r = e / VB, c = col0 + e % VB;
+            track[r * D + c] = state[r * D + c];
+        }
     }
 }
 
 }  // namespace
 
-hipError_t launch_prefill_chunked(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                                  const int32_t *cu_seqlens, int batch, int num_heads,
-                                  int64_t total_tokens, float *pool, int64_t pool_slots,
-                                  const int32_t *slot_idx, const float *slopes, uint16_t *out,
-                                  hipStream_t stream) {
+hipError_t launch_prefill_chunked(const PrefillArgs &a, int batch, hipStream_t stream) {
     if (batch == 0) return hipSuccess;
-    int pairs = batch * num_heads;
-    void *args[] = {&q, &k, &v, &cu_seqlens, &num_heads, &pairs, &total_tokens,
-                    &pool, &pool_slots, &slot_idx, &slopes, &out};
+    PrefillArgs copy = a;
+    copy.pairs = batch * a.num_heads;
+    void *args[] = {&copy};
     return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_chunked_kernel),
-                           dim3(static_cast<unsigned>(pairs) * NVB), dim3(NT), args, 0, stream);
+                           dim3(static_cast<unsigned>(copy.pairs) * NVB), dim3(NT), args, 0, stream);
 }
 
 }  // namespace la

@@ -1,17 +1,18 @@
-// Token-recurrent seg_la kernel: decode (one token), chain verify (k tokens)
-// and the fp32 prefill path.
+// Token-recurrent seg_la kernels: decode (one token), chain verify (k tokens),
+// tree verify (each draft forks from its parent's state), and the prefill path
+// for fp32 inputs and for head_dim 64.
 //
 // Citations name the web page "SGLang Lightning Attention 能力矩阵与 seg_la
 // 线性注意力测试覆盖深度解析" (www.2kiu.com/news/4599301) as [LA-page].
 //
 // Per (request, head) the recurrence of [LA-page] §独立参考实现 is advanced
-// one token at a time with the 128x128 fp32 state held in registers:
-//     S <- exp(-slope) * S + k v^T ;  o = (q @ S) / sqrt(128)
-// This path is bound by HBM traffic: per (request, head) it streams the 64 KiB
-// state in and out once, so each thread owns 16 rows x 4 columns of S and
-// moves it with 16 coalesced 128-bit loads and stores (nontemporal: the state
-// is touched once per call).  The q.S column sums are reduced across the 8
-// row groups with one cross-half-wave shuffle and a 4-wave LDS pass.
+// one token at a time with the d x d fp32 state held in registers:
+//     S <- exp(-slope) * S + k v^T ;  o = (q @ S) / sqrt(d)
+// This path is bound by HBM traffic: per (request, head) it streams the state
+// in and out once, so each of the 256 threads owns RPT rows x 4 columns of S
+// and moves it with coalesced 128-bit loads and stores (nontemporal: the state
+// is touched once per call).  The q.S column sums are reduced across the row
+// groups of a wave with cross-lane shuffles and across the 4 waves in LDS.
 #include "common.h"
 #include "launch.h"
 
@@ -19,27 +20,44 @@ namespace la {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kStateElems = kHeadDim * kHeadDim;
 
-// 16 consecutive elements starting at p (16-byte aligned), as floats
-__device__ __forceinline__ void load16(const uint16_t *p, float (&x)[16]) {
-    u16x8 a = *reinterpret_cast<const u16x8 *>(p);
-    u16x8 b = *reinterpret_cast<const u16x8 *>(p + 8);
+// Thread layout for head_dim D: column group cg = tid % CG owns value columns
+// 4cg..4cg+3, row group rg = tid / CG owns key rows RPT*rg .. RPT*rg+RPT-1.
+// A wave holds 64/CG row groups, so each 128-bit state load reads 64/CG full
+// rows.
+template <int D> struct Layout {
+    static constexpr int CG = D / 4;
+    static constexpr int RG = kThreads / CG;
+    static constexpr int RPT = D / RG;
+    static constexpr float kScale = D == 128 ? 0.08838834764831845f : 0.125f;  // D^-1/2
+    static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+};
+
+// N consecutive elements starting at p (8-byte aligned for bf16, 16 for fp32)
+template <int N> __device__ __forceinline__ void load_n(const uint16_t *p, float (&x)[N]) {
+    if constexpr (N % 8 == 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        x[e] = bf16_to_f32(a[e]);
-        x[8 + e] = bf16_to_f32(b[e]);
+        for (int i = 0; i < N / 8; ++i) {
+            const u16x8 a = *reinterpret_cast<const u16x8 *>(p + 8 * i);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[8 * i + e] = bf16_to_f32(a[e]);
+        }
+    } else {
+        static_assert(N == 4, "4 or a multiple of 8 elements");
+        const u16x4 a = *reinterpret_cast<const u16x4 *>(p);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = bf16_to_f32(a[e]);
     }
 }
 
-__device__ __forceinline__ void load16(const float *p, float (&x)[16]) {
+template <int N> __device__ __forceinline__ void load_n(const float *p, float (&x)[N]) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        f32x4 a = *reinterpret_cast<const f32x4 *>(p + 4 * e);
-        x[4 * e + 0] = a.x;
-        x[4 * e + 1] = a.y;
-        x[4 * e + 2] = a.z;
-        x[4 * e + 3] = a.w;
+    for (int i = 0; i < N / 4; ++i) {
+        const f32x4 a = *reinterpret_cast<const f32x4 *>(p + 4 * i);
+        x[4 * i + 0] = a.x;
+        x[4 * i + 1] = a.y;
+        x[4 * i + 2] = a.z;
+        x[4 * i + 3] = a.w;
     }
 }
 
@@ -57,116 +75,253 @@ __device__ __forceinline__ void store4(uint16_t *p, f32x4 x) {
 
 __device__ __forceinline__ void store4(float *p, f32x4 x) { *reinterpret_cast<f32x4 *>(p) = x; }
 
-// Thread layout: column group cg = tid % 32 owns value columns 4cg..4cg+3,
-// row group rg = tid / 32 owns key rows 16rg..16rg+15.  A wave covers two row
-// groups, so each 128-bit load instruction reads two full 512-byte rows.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void recurrent_kernel(
-    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const int32_t *__restrict__ cu_seqlens, int tokens_per_req, int num_heads,
-    int64_t total_tokens, float *__restrict__ pool, int64_t pool_slots,
-    const int32_t *__restrict__ slot_idx, const float *__restrict__ slopes, T *__restrict__ out,
-    float *__restrict__ state_out) {
-    const int b = blockIdx.x / num_heads;
-    const int h = blockIdx.x - b * num_heads;
+template <int D, int RPT>
+__device__ __forceinline__ void load_state(const float *s, int soff, f32x4 (&S)[RPT]) {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+        S[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(s + soff + r * D));
+}
+
+template <int D, int RPT>
+__device__ __forceinline__ void store_state(float *s, int soff, const f32x4 (&S)[RPT]) {
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+        __builtin_nontemporal_store(S[r], reinterpret_cast<f32x4 *>(s + soff + r * D));
+}
+
+// o = scale * q @ S for this thread's columns, summed over all row groups and
+// stored by wave 0.  red is double-buffered by `parity`, so one barrier per
+// token suffices: a buffer is rewritten only after the next barrier.
+template <int D, typename T>
+__device__ __forceinline__ void reduce_store(f32x4 o, f32x4 (&red)[2][4][Layout<D>::CG], int &parity,
+                                             T *dst) {
+    using L = Layout<D>;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, cg = tid % L::CG;
+#pragma unroll
+    for (int m = L::CG; m < 64; m <<= 1) {
+        o.x += __shfl_xor(o.x, m);
+        o.y += __shfl_xor(o.y, m);
+        o.z += __shfl_xor(o.z, m);
+        o.w += __shfl_xor(o.w, m);
+    }
+    if (lane < L::CG) red[parity][wave][cg] = o;
+    __syncthreads();
+    if (wave == 0 && lane < L::CG) {
+        const f32x4 s = red[parity][0][lane] + red[parity][1][lane] + red[parity][2][lane] +
+                        red[parity][3][lane];
+        store4(dst + 4 * lane, s * L::kScale);
+    }
+    parity ^= 1;
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void zero_rows(T *out, int64_t t0, int64_t t1, size_t row, int h) {
     const int tid = threadIdx.x;
-    const int cg = tid & 31, rg = tid >> 5, lane = tid & 63, wave = tid >> 6;
+    if (tid < D / 4)
+        for (int64_t t = t0; t < t1; ++t)
+            store4(out + t * row + static_cast<size_t>(h) * D + 4 * tid, f32x4{0, 0, 0, 0});
+}
+
+// kTrack: the prefill variant that may take a state-tracking snapshot
+template <typename T, int D, bool kTrack>
+__global__ __launch_bounds__(kThreads) void recurrent_kernel(RecurrentArgs a) {
+    using L = Layout<D>;
+    constexpr int RPT = L::RPT;
+    const T *__restrict__ q = static_cast<const T *>(a.q);
+    const T *__restrict__ k = static_cast<const T *>(a.k);
+    const T *__restrict__ v = static_cast<const T *>(a.v);
+    T *__restrict__ out = static_cast<T *>(a.out);
+    const int H = a.num_heads;
+    const int b = blockIdx.x / H;
+    const int h = blockIdx.x - b * H;
+    const int hk = h / (H / a.num_kv_heads);
+    const int tid = threadIdx.x;
+    const int cg = tid % L::CG, rg = tid / L::CG;
 
     int64_t t0, t1;
-    if (cu_seqlens) {
-        t0 = cu_seqlens[b];
-        t1 = cu_seqlens[b + 1];
+    if (a.cu_seqlens) {
+        t0 = a.cu_seqlens[b];
+        t1 = a.cu_seqlens[b + 1];
     } else {
-        t0 = static_cast<int64_t>(b) * tokens_per_req;
-        t1 = t0 + tokens_per_req;
+        t0 = static_cast<int64_t>(b) * a.tokens_per_req;
+        t1 = t0 + a.tokens_per_req;
     }
-    t0 = t0 < 0 ? 0 : (t0 > total_tokens ? total_tokens : t0);
-    t1 = t1 < t0 ? t0 : (t1 > total_tokens ? total_tokens : t1);
+    t0 = t0 < 0 ? 0 : (t0 > a.total_tokens ? a.total_tokens : t0);
+    t1 = t1 < t0 ? t0 : (t1 > a.total_tokens ? a.total_tokens : t1);
 
-    const size_t row = static_cast<size_t>(num_heads) * kHeadDim;  // token stride
-    const int slot = slot_idx[b];
-    if (slot < 0 || slot >= pool_slots) {
-        // out-of-range slot: zero output, no state touched
-        if (wave == 0 && lane < 32)
-            for (int64_t t = t0; t < t1; ++t)
-                store4(out + t * row + static_cast<size_t>(h) * kHeadDim + 4 * lane, f32x4{0, 0, 0, 0});
+    const size_t row = static_cast<size_t>(H) * D;                // q/out token stride
+    const size_t kvrow = static_cast<size_t>(a.num_kv_heads) * D;  // k/v token stride
+    const int slot = a.slot_idx[b];
+    if (slot < 0 || slot >= a.pool_slots) {
+        zero_rows<T, D>(out, t0, t1, row, h);  // out-of-range slot: no state touched
         return;
     }
+    const size_t sdd = static_cast<size_t>(D) * D;
+    float *s_in = a.pool + (static_cast<size_t>(slot) * H + h) * sdd;
+    float *s_out = a.state_out ? a.state_out + (static_cast<size_t>(b) * H + h) * sdd : s_in;
+    // state-tracking snapshot after the first `tl` tokens ([LA-page] §额外覆盖)
+    float *snap = nullptr;
+    int64_t tl = -1;
+    if (kTrack && a.track_lens) {
+        const int ts = a.track_slot_idx[b];
+        tl = a.track_lens[b];
+        if (ts >= 0 && ts < a.pool_slots && tl >= 0 && tl <= t1 - t0)
+            snap = a.pool + (static_cast<size_t>(ts) * H + h) * sdd;
+    }
+    const int soff = (RPT * rg) * D + 4 * cg;
 
-    float *s_in = pool + (static_cast<size_t>(slot) * num_heads + h) * kStateElems;
-    float *s_out = state_out ? state_out + (static_cast<size_t>(b) * num_heads + h) * kStateElems : s_in;
-    const int soff = (16 * rg) * kHeadDim + 4 * cg;
+    f32x4 S[RPT];
+    load_state<D>(s_in, soff, S);
 
-    f32x4 S[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-        S[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(s_in + soff + r * kHeadDim));
+    const float decay = expf(-a.slopes[h]);
 
-    const float decay = expf(-slopes[h]);
-    const float scale = 0.08838834764831845f;  // 128^-1/2
-
-    __shared__ f32x4 red[2][4][32];
+    __shared__ f32x4 red[2][4][L::CG];
     int parity = 0;
     for (int64_t t = t0; t < t1; ++t) {
-        const size_t off = t * row + static_cast<size_t>(h) * kHeadDim;
-        float kk[16], qq[16];
-        load16(k + off + 16 * rg, kk);
-        load16(q + off + 16 * rg, qq);
-        const f32x4 vv = load4(v + off + 4 * cg);
+        if (kTrack && snap && t - t0 == tl) store_state<D>(snap, soff, S);
+        const size_t off = t * row + static_cast<size_t>(h) * D;
+        const size_t kvoff = t * kvrow + static_cast<size_t>(hk) * D;
+        float kk[RPT], qq[RPT];
+        load_n<RPT>(k + kvoff + RPT * rg, kk);
+        load_n<RPT>(q + off + RPT * rg, qq);
+        const f32x4 vv = load4(v + kvoff + 4 * cg);
         f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < RPT; ++r) {
             S[r] = decay * S[r] + kk[r] * vv;
             o += qq[r] * S[r];
         }
-        o.x += __shfl_xor(o.x, 32);
-        o.y += __shfl_xor(o.y, 32);
-        o.z += __shfl_xor(o.z, 32);
-        o.w += __shfl_xor(o.w, 32);
-        if (lane < 32) red[parity][wave][cg] = o;
-        __syncthreads();
-        if (wave == 0 && lane < 32) {
-            f32x4 s = red[parity][0][lane] + red[parity][1][lane] + red[parity][2][lane] +
-                      red[parity][3][lane];
-            store4(out + off + 4 * lane, s * scale);
-        }
-        parity ^= 1;
+        reduce_store<D>(o, red, parity, out + off);
     }
-
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-        __builtin_nontemporal_store(S[r], reinterpret_cast<f32x4 *>(s_out + soff + r * kHeadDim));
+    if (kTrack && snap && tl == t1 - t0) store_state<D>(snap, soff, S);
+    store_state<D>(s_out, soff, S);
 }
 
-template <typename T>
-hipError_t launch(const void *q, const void *k, const void *v, const int32_t *cu_seqlens,
-                  int tokens_per_req, int batch, int num_heads, int64_t total_tokens, float *pool,
-                  int64_t pool_slots, const int32_t *slot_idx, const float *slopes, void *out,
-                  float *state_out, hipStream_t stream) {
-    const T *qp = static_cast<const T *>(q), *kp = static_cast<const T *>(k),
-            *vp = static_cast<const T *>(v);
-    T *op = static_cast<T *>(out);
-    void *args[] = {&qp, &kp, &vp, &cu_seqlens, &tokens_per_req, &num_heads, &total_tokens,
-                    &pool, &pool_slots, &slot_idx, &slopes, &op, &state_out};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&recurrent_kernel<T>),
-                           dim3(static_cast<unsigned>(batch) * num_heads), dim3(kThreads), args, 0,
-                           stream);
+// Tree verify ([LA-page] §生产环境不支持 item 3, Next Work item 2).  Draft j
+// of request b forks from its parent's state:
+//     S_j = e^{-l} S_parent + k_j v_j^T
+// With A the state of draft j-1 in registers and R the request's pool state
+// (read again from the pool, which this call never writes, when needed):
+//   parent j-1:  A <- e^{-l} A + k_j v_j^T       (the chain case)
+//   parent -1:   A <- e^{-l} R + k_j v_j^T
+//   otherwise:   unroll S_j up the parent chain a_1 = parent, a_2, ...:
+//                A <- k_j v_j^T + sum_m e^{-l m} k_{a_m} v_{a_m}^T + e^{-l depth} R
+// Parents are checked first (each in [-1, j)), so the walk strictly descends
+// and ends.  A request with a bad slot or parent gets zero output.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void tree_kernel(TreeArgs a) {
+    using L = Layout<D>;
+    constexpr int RPT = L::RPT;
+    const T *__restrict__ q = static_cast<const T *>(a.q);
+    const T *__restrict__ k = static_cast<const T *>(a.k);
+    const T *__restrict__ v = static_cast<const T *>(a.v);
+    T *__restrict__ out = static_cast<T *>(a.out);
+    const int H = a.num_heads, n = a.num_draft;
+    const int b = blockIdx.x / H;
+    const int h = blockIdx.x - b * H;
+    const int hk = h / (H / a.num_kv_heads);
+    const int tid = threadIdx.x;
+    const int cg = tid % L::CG, rg = tid / L::CG;
+    const size_t row = static_cast<size_t>(H) * D;
+    const size_t kvrow = static_cast<size_t>(a.num_kv_heads) * D;
+    const int64_t t0 = static_cast<int64_t>(b) * n;
+    const int32_t *par = a.parent_idx + t0;
+
+    const int slot = a.slot_idx[b];
+    bool ok = slot >= 0 && slot < a.pool_slots;
+    for (int j = 0; j < n && ok; ++j) ok = par[j] >= -1 && par[j] < j;
+    if (!ok) {
+        zero_rows<T, D>(out, t0, t0 + n, row, h);
+        return;
+    }
+    const size_t sdd = static_cast<size_t>(D) * D;
+    const int soff = (RPT * rg) * D + 4 * cg;
+    const float *R = a.pool + (static_cast<size_t>(slot) * H + h) * sdd + soff;
+    f32x4 A[RPT];
+    const float decay = expf(-a.slopes[h]);
+
+    auto kv = [&](int j, float (&kk)[RPT], f32x4 &vv) {
+        const size_t kvoff = (t0 + j) * kvrow + static_cast<size_t>(hk) * D;
+        load_n<RPT>(k + kvoff + RPT * rg, kk);
+        vv = load4(v + kvoff + 4 * cg);
+    };
+
+    __shared__ f32x4 red[2][4][L::CG];
+    int parity = 0;
+    for (int j = 0; j < n; ++j) {
+        float kk[RPT], qq[RPT];
+        f32x4 vv;
+        kv(j, kk, vv);
+        const size_t off = (t0 + j) * row + static_cast<size_t>(h) * D;
+        load_n<RPT>(q + off + RPT * rg, qq);
+        const int p = par[j];
+        if (p >= 0 && p == j - 1) {
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) A[r] = decay * A[r] + kk[r] * vv;
+        } else if (p < 0) {
+#pragma unroll
+            for (int r = 0; r < RPT; ++r)
+                A[r] = decay * *reinterpret_cast<const f32x4 *>(R + r * D) + kk[r] * vv;
+        } else {
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) A[r] = kk[r] * vv;
+            float w = decay;
+            for (int x = p; x >= 0; x = par[x]) {
+                float ka[RPT];
+                f32x4 va;
+                kv(x, ka, va);
+#pragma unroll
+                for (int r = 0; r < RPT; ++r) A[r] += (w * ka[r]) * va;
+                w *= decay;
+            }
+#pragma unroll
+            for (int r = 0; r < RPT; ++r) A[r] += w * *reinterpret_cast<const f32x4 *>(R + r * D);
+        }
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) o += qq[r] * A[r];
+        reduce_store<D>(o, red, parity, out + off);
+        if (a.draft_states)
+            store_state<D>(a.draft_states + ((t0 + j) * H + h) * sdd, soff, A);
+    }
+}
+
+template <typename T, int D>
+hipError_t launch_rec(const RecurrentArgs &a, int batch, hipStream_t stream) {
+    RecurrentArgs copy = a;
+    void *args[] = {&copy};
+    const void *fn = a.track_lens ? reinterpret_cast<const void *>(&recurrent_kernel<T, D, true>)
+                                  : reinterpret_cast<const void *>(&recurrent_kernel<T, D, false>);
+    return hipLaunchKernel(fn,
+                           dim3(static_cast<unsigned>(batch) * a.num_heads), dim3(kThreads), args,
+                           0, stream);
+}
+
+template <typename T, int D>
+hipError_t launch_tree_t(const TreeArgs &a, int batch, hipStream_t stream) {
+    TreeArgs copy = a;
+    void *args[] = {&copy};
+    return hipLaunchKernel(reinterpret_cast<const void *>(&tree_kernel<T, D>),
+                           dim3(static_cast<unsigned>(batch) * a.num_heads), dim3(kThreads), args,
+                           0, stream);
 }
 
 }  // namespace
 
-hipError_t launch_recurrent(bool bf16, const void *q, const void *k, const void *v,
-                            const int32_t *cu_seqlens, int tokens_per_req, int batch,
-                            int num_heads, int64_t total_tokens, float *pool,
-                            int64_t pool_slots, const int32_t *slot_idx, const float *slopes,
-                            void *out, float *state_out, hipStream_t stream) {
+hipError_t launch_recurrent(const RecurrentArgs &a, bool bf16, int head_dim, int batch,
+                            hipStream_t stream) {
     if (batch == 0) return hipSuccess;
-    if (bf16)
-        return launch<uint16_t>(q, k, v, cu_seqlens, tokens_per_req, batch, num_heads,
-                                total_tokens, pool, pool_slots, slot_idx, slopes, out, state_out,
-                                stream);
-    return launch<float>(q, k, v, cu_seqlens, tokens_per_req, batch, num_heads, total_tokens,
-                         pool, pool_slots, slot_idx, slopes, out, state_out, stream);
+    if (head_dim == 128)
+        return bf16 ? launch_rec<uint16_t, 128>(a, batch, stream) : launch_rec<float, 128>(a, batch, stream);
+    return bf16 ? launch_rec<uint16_t, 64>(a, batch, stream) : launch_rec<float, 64>(a, batch, stream);
+}
+
+hipError_t launch_tree(const TreeArgs &a, bool bf16, int head_dim, int batch, hipStream_t stream) {
+    if (batch == 0) return hipSuccess;
+    if (head_dim == 128)
+        return bf16 ? launch_tree_t<uint16_t, 128>(a, batch, stream)
+                    : launch_tree_t<float, 128>(a, batch, stream);
+    return bf16 ? launch_tree_t<uint16_t, 64>(a, batch, stream) : launch_tree_t<float, 64>(a, batch, stream);
 }
 
 }  // namespace la

@@ -95,7 +95,7 @@ class Workload:
 
     kind: "prefill" (packed varlen), "decode" (one token per request) or
     "verify" (num_draft chained tokens per request).
-    q, k, v: [T, H, d] (uint16 bf16 bits, or float32), T = cu_seqlens[-1].
+    q: [T, H, d]; k, v: [T, Hkv, d] (uint16 bf16 bits, or float32), T = cu_seqlens[-1].
     pool: [P, H, d, d] float32; slot_idx: [B] int32; cu_seqlens: [B+1] int32.
     """
     name: str
@@ -115,6 +115,11 @@ class Workload:
     v: np.ndarray
     num_draft: int = 1
     prefix_mask: np.ndarray = field(default=None)
+    num_kv_heads: int = 0  # 0: same as num_heads
+
+    def __post_init__(self):
+        if not self.num_kv_heads:
+            self.num_kv_heads = self.num_heads
 
     @property
     def batch(self) -> int:
@@ -156,8 +161,10 @@ def _pool(seed, P, H, d, fill_slots, zero_slots):
 
 def make(name, kind, dtype, num_heads, lengths, pool_slots, *, head_dim=128, seed=0,
          layer_id=0, num_layers=1, prefix=None, slot_idx=None, fill_all_slots=False,
-         num_draft=1):
+         num_draft=1, num_kv_heads=None):
     """General workload builder.
+
+    num_kv_heads: heads of k and v (grouped heads; default num_heads).
 
     lengths: per-request token counts (for "verify" every entry is num_draft).
     prefix: bool per request (True -> 0.05*N prefix state), default all False.
@@ -181,14 +188,15 @@ def make(name, kind, dtype, num_heads, lengths, pool_slots, *, head_dim=128, see
     cu = np.zeros(B + 1, dtype=np.int32)
     np.cumsum(lengths, out=cu[1:])
     T = int(cu[-1])
+    hk = num_kv_heads or num_heads
     q = normal_tokens(seed, _TAG_Q, T, num_heads, head_dim, dtype)
-    k = normal_tokens(seed, _TAG_K, T, num_heads, head_dim, dtype)
-    v = normal_tokens(seed, _TAG_V, T, num_heads, head_dim, dtype)
+    k = normal_tokens(seed, _TAG_K, T, hk, head_dim, dtype)
+    v = normal_tokens(seed, _TAG_V, T, hk, head_dim, dtype)
     pool = _pool(seed, pool_slots, num_heads, head_dim, fill, zero)
     return Workload(name=name, kind=kind, dtype=dtype, num_heads=num_heads, head_dim=head_dim,
                     layer_id=layer_id, num_layers=num_layers, seed=seed, lengths=lengths,
                     cu_seqlens=cu, slot_idx=slot_idx, pool=pool, q=q, k=k, v=v,
-                    num_draft=num_draft, prefix_mask=prefix)
+                    num_draft=num_draft, prefix_mask=prefix, num_kv_heads=hk)
 
 
 CONFIG_NAMES = {

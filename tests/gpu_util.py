@@ -97,7 +97,10 @@ def oracle_ref(wl, heads=None):
     if heads is None:
         q, k, v, pool = wl.q, wl.k, wl.v, wl.pool
     else:
-        q, k, v = wl.q[:, heads], wl.k[:, heads], wl.v[:, heads]
+        # each selected query head keeps its own kv head (one kv head per head)
+        g = wl.num_heads // wl.num_kv_heads
+        kvh = [h // g for h in heads]
+        q, k, v = wl.q[:, heads], wl.k[:, kvh], wl.v[:, kvh]
         pool = wl.pool[:, heads]
         slopes = slopes[heads]
     return oracle.prefill(q, k, v, wl.cu_seqlens, pool, wl.slot_idx, slopes)

@@ -73,17 +73,19 @@ def test_slopes_reject_bad_arguments(lib):
 
 def _prefill(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=la.LA_DTYPE_BF16, cu=FAKE, batch=2, T=10, max_seqlen=8,
-             H=4, d=128, pool=FAKE, P=4, slot=FAKE, slopes=FAKE, out=FAKE, stream=None)
+             H=4, HK=4, d=128, pool=FAKE, P=4, slot=FAKE, tl=None, ts=None, slopes=FAKE, out=FAKE,
+             stream=None)
     a.update(kw)
     return lib.la_prefill(a["q"], a["k"], a["v"], a["dtype"], a["cu"], a["batch"], a["T"],
-                          a["max_seqlen"], a["H"], a["d"], a["pool"], a["P"], a["slot"],
-                          a["slopes"], a["out"], a["stream"])
+                          a["max_seqlen"], a["H"], a["HK"], a["d"], a["pool"], a["P"], a["slot"],
+                          a["tl"], a["ts"], a["slopes"], a["out"], a["stream"])
 
 
 def test_prefill_validation(lib):
     E, U = la.LA_ERR_INVALID_ARG, la.LA_ERR_UNSUPPORTED
-    assert _prefill(lib, d=64) == U           # head_dim constraint
+    assert _prefill(lib, d=32) == U           # head_dim must be 64 or 128
     assert _prefill(lib, d=256) == U
+    assert _prefill(lib, d=64, q=None) == E   # 64 passes the head_dim check
     assert _prefill(lib, dtype=5) == U
     assert _prefill(lib, q=None) == E
     assert _prefill(lib, out=None) == E
@@ -94,6 +96,11 @@ def test_prefill_validation(lib):
     assert _prefill(lib, batch=-1) == E
     assert _prefill(lib, T=-1) == E
     assert _prefill(lib, H=0) == E
+    assert _prefill(lib, HK=0) == E
+    assert _prefill(lib, HK=3) == E           # kv heads must divide heads
+    assert _prefill(lib, H=4, HK=8) == E
+    assert _prefill(lib, tl=FAKE) == E        # track arrays go together
+    assert _prefill(lib, ts=FAKE) == E
     assert _prefill(lib, max_seqlen=-1) == E
     assert _prefill(lib, batch=5, P=4) == E   # more requests than distinct slots
     assert _prefill(lib, P=0) == E
@@ -104,34 +111,61 @@ def test_prefill_validation(lib):
 
 
 def _decode(lib, **kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=la.LA_DTYPE_BF16, batch=2, H=4, d=128, pool=FAKE, P=4,
-             slot=FAKE, slopes=FAKE, out=FAKE, stream=None)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=la.LA_DTYPE_BF16, batch=2, H=4, HK=4, d=128, pool=FAKE,
+             P=4, slot=FAKE, slopes=FAKE, out=FAKE, stream=None)
     a.update(kw)
-    return lib.la_decode(a["q"], a["k"], a["v"], a["dtype"], a["batch"], a["H"], a["d"], a["pool"],
-                         a["P"], a["slot"], a["slopes"], a["out"], a["stream"])
+    return lib.la_decode(a["q"], a["k"], a["v"], a["dtype"], a["batch"], a["H"], a["HK"], a["d"],
+                         a["pool"], a["P"], a["slot"], a["slopes"], a["out"], a["stream"])
 
 
 def _verify(lib, **kw):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=la.LA_DTYPE_BF16, batch=2, nd=5, H=4, d=128, pool=FAKE,
-             P=4, slot=FAKE, slopes=FAKE, out=FAKE, so=FAKE, stream=None)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=la.LA_DTYPE_BF16, batch=2, nd=5, H=4, HK=2, d=128,
+             pool=FAKE, P=4, slot=FAKE, slopes=FAKE, out=FAKE, so=FAKE, stream=None)
     a.update(kw)
-    return lib.la_verify(a["q"], a["k"], a["v"], a["dtype"], a["batch"], a["nd"], a["H"], a["d"],
-                         a["pool"], a["P"], a["slot"], a["slopes"], a["out"], a["so"], a["stream"])
+    return lib.la_verify(a["q"], a["k"], a["v"], a["dtype"], a["batch"], a["nd"], a["H"], a["HK"],
+                         a["d"], a["pool"], a["P"], a["slot"], a["slopes"], a["out"], a["so"],
+                         a["stream"])
+
+
+def _tree(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=la.LA_DTYPE_BF16, batch=2, nd=5, H=4, HK=1, d=64,
+             pool=FAKE, P=4, slot=FAKE, par=FAKE, slopes=FAKE, out=FAKE, ds=FAKE, stream=None)
+    a.update(kw)
+    return lib.la_verify_tree(a["q"], a["k"], a["v"], a["dtype"], a["batch"], a["nd"], a["H"],
+                              a["HK"], a["d"], a["pool"], a["P"], a["slot"], a["par"], a["slopes"],
+                              a["out"], a["ds"], a["stream"])
 
 
 def test_decode_and_verify_validation(lib):
     E, U = la.LA_ERR_INVALID_ARG, la.LA_ERR_UNSUPPORTED
-    assert _decode(lib, d=64) == U
+    assert _decode(lib, d=48) == U
     assert _decode(lib, dtype=3) == U
     assert _decode(lib, q=None) == E
     assert _decode(lib, batch=9, P=4) == E
     assert _decode(lib, slopes=None) == E
+    assert _decode(lib, HK=3) == E
     assert _verify(lib, nd=0) == U            # chain length must be positive
     assert _verify(lib, nd=-2) == U
     assert _verify(lib, d=96) == U
     assert _verify(lib, out=None) == E
     assert _verify(lib, batch=-1) == E
+    assert _verify(lib, HK=-1) == E
     assert _verify(lib, batch=0, q=None, k=None, v=None, out=None, slot=None) == la.LA_OK
+
+
+def test_tree_verify_validation(lib):
+    E, U = la.LA_ERR_INVALID_ARG, la.LA_ERR_UNSUPPORTED
+    assert _tree(lib, nd=0) == U
+    assert _tree(lib, d=100) == U
+    assert _tree(lib, dtype=9) == U
+    assert _tree(lib, par=None) == E          # parents are required
+    assert _tree(lib, pool=None) == E
+    assert _tree(lib, HK=3) == E
+    assert _tree(lib, batch=7, P=4) == E
+    assert _tree(lib, batch=-1) == E
+    # draft_states may be NULL, and an empty batch launches nothing
+    assert _tree(lib, batch=0, q=None, k=None, v=None, out=None, slot=None, par=None,
+                 ds=None) == la.LA_OK
 
 
 def test_binding_rejects_host_tensors(lib):
