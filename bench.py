@@ -50,6 +50,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = {
     "prefill_chunked_kernel": ["prefill_chunked.hip", "common.h"],
     "recurrent_kernel<bf16>": ["recurrent.hip", "common.h"],
+    "tree_kernel<bf16>": ["recurrent.hip", "common.h"],
 }
 
 
@@ -341,7 +342,8 @@ def main():
             "config": {"batch": wv.batch, "num_draft": wv.num_draft, "num_heads": H,
                        "tree": "seeded random parents in [-1, j)", "draft_states": True},
             "roofline": {"bound": "hbm", "achieved": t_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": t_gbs / HBM_PEAK_GBS, "traffic": None,
+                         "frac": t_gbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("tree_kernel<bf16>", "tree-verify"),
                          "kernel": "tree_kernel<bf16>", "algorithmic_bytes": tb},
         },
         "decode_graph": graph,

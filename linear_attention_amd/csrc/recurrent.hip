@@ -201,7 +201,9 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(RecurrentArgs a) {
 // of request b forks from its parent's state:
 //     S_j = e^{-l} S_parent + k_j v_j^T
 // With A the state of draft j-1 in registers and R the request's pool state
-// (read again from the pool, which this call never writes, when needed):
+// (read where it is needed with cached loads: this call never writes the pool,
+// and the repeat reads mostly hit in cache; a copy kept in registers or LDS
+// measured slower):
 //   parent j-1:  A <- e^{-l} A + k_j v_j^T       (the chain case)
 //   parent -1:   A <- e^{-l} R + k_j v_j^T
 //   otherwise:   unroll S_j up the parent chain a_1 = parent, a_2, ...:
