@@ -19,17 +19,21 @@
 // an exact bf16 input to ~2^-17 relative error; without it the bf16 rounding
 // of P, S_prev and Vd each add output errors of order 1e-2 on small-slope heads.
 //
-// Work split.  One workgroup of 4 waves per (request, head, 32-column block of
-// S); the block id is mapped so the 4 column blocks of a head share an XCD
-// (ids are dealt to the 8 XCDs round-robin) and its L2 serves their repeated
-// Q/K reads.  Wave w keeps the fp32 state rows 32w..32w+31 of the block in
-// MFMA accumulators for the whole request.  Per chunk every wave computes
-//   * the inter term restricted to its own 32 state rows, for all 64 tokens,
-//     straight from its accumulators (no state exchange),
-//   * a balanced share of the 10 causal score tiles and their P V products,
-//   * the update of its own state rows,
-// and the four partial O^T tiles of each 16-token row block are summed through
-// LDS by the wave that stores them.
+// Work split.  One workgroup of 8 waves (two per SIMD) per (request, head,
+// 32-column block of S); the block id is mapped so the 4 column blocks of a
+// head share an XCD (ids are dealt to the 8 XCDs round-robin) and its L2 serves
+// their repeated Q/K reads.  The waves take two roles, so that each fits in
+// half of a SIMD's registers and the SIMD can overlap one wave's MFMAs with the
+// other's vector and LDS work:
+//   * state wave s (0..3) keeps the fp32 state rows 32s..32s+31 of the block in
+//     MFMA accumulators for the whole request; per chunk it computes the inter
+//     term of all 64 tokens restricted to its rows (no state exchange) and the
+//     update of its rows, and it sums and stores the output of row block s;
+//   * score wave w (0..3) computes a balanced share of the 10 causal score
+//     tiles and their P V products, stages a quarter of every chunk, and
+//     decays a quarter of the next chunk's V.
+// The partial O^T tiles meet in LDS, where the state wave of each 16-token row
+// block adds them up.
 //
 // Data movement.  Q, K and V tiles are copied from global memory straight
 // into a 3-deep LDS staging ring (global_load_lds_dwordx4: lane L of a wave
@@ -60,7 +64,7 @@ constexpr int D = kHeadDim;  // 128
 constexpr int C = 64;        // chunk length
 constexpr int VB = 32;       // state columns per workgroup
 constexpr int NVB = D / VB;  // column blocks per head
-constexpr int NT = 256;      // threads per workgroup
+constexpr int NT = 512;      // threads per workgroup: 4 state + 4 score waves
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -93,7 +97,8 @@ struct Smem {
     uint16_t v[NBUF][C * VB];
     uint16_t vd_hi[C * VB];   // decayed V of the current chunk, hi/lo
     uint16_t vd_lo[C * VB];
-    f32x4 part[4][4][2][64];  // [source wave][row block][column tile][lane]
+    f32x4 inter[4][3][2][64]; // [state wave][other row block][column tile][lane]
+    f32x4 intra[4][2][2][64]; // [score wave][tile group][column tile][lane]
 };
 
 __device__ __forceinline__ f32x4 mma(u16x8 a, u16x8 b, f32x4 c) {
@@ -205,45 +210,27 @@ template <> struct Tiles<3> {
 // and every factor stays inside the fp32/bf16 exponent range for l <= 2.
 // Without kF the weights e^{-l(i-j)} and e^{-l(i+1)} are applied directly.
 
-// One chunk for wave W: produce the partial O^T tiles part[it][nt] and
-// advance this wave's state rows S[mt][nt].  mdec[4t + r]: weight of score
-// tile t element r; qdec[it]: weight of the inter term for i = 16 it + l16
-// (only used without kF); dc: e^{-l c}.
-//
-// The work is laid out in stages separated by scheduling barriers so that
-// every group of LDS fragment reads is issued well before the MFMAs that
-// consume it: its latency is covered by VALU work (state and score splits)
-// or by the previous group's MFMAs.
-template <int W, bool kF>
-__device__ __forceinline__ void chunk_compute(const uint16_t *sq, const uint16_t *sk, const uint16_t *sv,
-                                              const uint16_t *svh, const uint16_t *svl,
-                                              const float (&mdec)[12], const float (&qdec)[4], float dc,
-                                              int g, int l16, f32x4 (&S)[2][2], f32x4 (&part)[4][2]) {
-    using T = Tiles<W>;
+// One chunk for state wave SW: the inter term of all 64 tokens restricted to
+// state rows 32SW..32SW+31, part[it][nt], and the update of those rows,
+// S[k][v] = e^{-l c} S + sum_j K[j][k] Vd[j][v].  qdec[it]: weight of the inter
+// term for token i = 16 it + l16 (only without kF); dc: e^{-l c}.
+template <int SW, bool kF>
+__device__ __forceinline__ void state_chunk(const uint16_t *sq, const uint16_t *sk, const uint16_t *svh,
+                                            const uint16_t *svl, const float (&qdec)[4], float dc, int g,
+                                            int l16, f32x4 (&S)[2][2], f32x4 (&part)[4][2]) {
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    const u16x4 z4 = {0, 0, 0, 0};
 
-    // stage 1: fragments of the inter term (Q^T restricted to this wave's 32
-    // state rows, all four row blocks) and of the score tiles
+    // Q^T restricted to this wave's rows (B operand: lane (g, l16) holds token
+    // 16 it + l16 and features 32SW + 4g + r, 32SW + 16 + 4g + r, the order in
+    // which the state rows sit in the A operand below)
     u16x8 qb[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int qr = 16 * it + l16;
-        qb[it] = cat(lds4(&sq[qk_off(qr, 32 * W + 4 * g)]), lds4(&sq[qk_off(qr, 32 * W + 16 + 4 * g)]));
+        qb[it] = cat(lds4(&sq[qk_off(qr, 32 * SW + 4 * g)]), lds4(&sq[qk_off(qr, 32 * SW + 16 + 4 * g)]));
     }
-    u16x8 kf[2][4], qf[2][4];
-#pragma unroll
-    for (int a = 0; a < T::nj; ++a)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) kf[a][s] = lds8(&sk[qk_off(16 * T::jl[a] + l16, 32 * s + 8 * g)]);
-#pragma unroll
-    for (int b = 0; b < T::ni; ++b)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) qf[b][s] = lds8(&sq[qk_off(16 * T::il[b] + l16, 32 * s + 8 * g)]);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // stage 2: the state as bf16 hi/lo A operand (v x k): lane (g, l16) holds
-    // rows k = 32W + 4g + r (mt 0) and 32W + 16 + 4g + r (mt 1) of column v = l16
+    // the state as bf16 hi/lo A operand (v x k): lane (g, l16) holds rows
+    // k = 32SW + 4g + r (mt 0) and 32SW + 16 + 4g + r (mt 1) of column v = l16
     u16x8 sa_hi[2], sa_lo[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
@@ -255,7 +242,7 @@ __device__ __forceinline__ void chunk_compute(const uint16_t *sq, const uint16_t
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // stage 3: inter term O^T[v][i] = sum_k S^T[v][k] Q^T[k][i] over this wave's rows
+    // inter term O^T[v][i] = sum_k S^T[v][k] Q^T[k][i] over this wave's rows
 #pragma unroll
     for (int it = 0; it < 4; ++it)
 #pragma unroll
@@ -264,95 +251,35 @@ __device__ __forceinline__ void chunk_compute(const uint16_t *sq, const uint16_t
             acc = mma(sa_lo[nt], qb[it], acc);
             part[it][nt] = kF ? acc : acc * qdec[it];
         }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // stage 4: issue the V^T fragments of the P V products and the first half
-    // of the state-update fragments, then the score MFMAs
-    u16x8 av[2][2];
-#pragma unroll
-    for (int q = 0; q < T::ng; ++q) {
-        const int ta = T::ga[q], tb = T::gb[q];
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-            av[q][nt] = cat(ldtr_v(sv, 16 * T::jl[T::tj[ta]], 16 * nt, g, l16),
-                            tb >= 0 ? ldtr_v(sv, 16 * T::jl[T::tj[tb]], 16 * nt, g, l16) : z4);
-    }
+    // fragments of the update: K^T rows of this wave and the decayed V, with
+    // tokens along the contraction
     u16x8 ka[2][2], vh[2][2], vl[2][2];
-    auto kv_frags = [&](int s2) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
-            ka[s2][mt] = cat(ldtr_qk(sk, 32 * s2, 32 * W + 16 * mt, g, l16),
-                             ldtr_qk(sk, 32 * s2 + 16, 32 * W + 16 * mt, g, l16));
+            ka[s2][mt] = cat(ldtr_qk(sk, 32 * s2, 32 * SW + 16 * mt, g, l16),
+                             ldtr_qk(sk, 32 * s2 + 16, 32 * SW + 16 * mt, g, l16));
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             vh[s2][nt] = cat(ldtr_v(svh, 32 * s2, 16 * nt, g, l16), ldtr_v(svh, 32 * s2 + 16, 16 * nt, g, l16));
             vl[s2][nt] = cat(ldtr_v(svl, 32 * s2, 16 * nt, g, l16), ldtr_v(svl, 32 * s2 + 16, 16 * nt, g, l16));
         }
-    };
-    kv_frags(0);
-    f32x4 sc[3];
-#pragma unroll
-    for (int t = 0; t < T::n; ++t) sc[t] = z;
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int t = 0; t < T::n; ++t) sc[t] = mma(kf[T::tj[t]][s], qf[T::ti[t]][s], sc[t]);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // stage 5: weight, mask and split the scores (A^T[j][i] = k_j . q_i)
-    u16x4 p_hi[3], p_lo[3];
-#pragma unroll
-    for (int t = 0; t < T::n; ++t) {
-        f32x4 p;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[r] = sc[t][r] * mdec[4 * t + r];
-        split4(p, p_hi[t], p_lo[t]);
     }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // stage 6: intra term O^T[v][i] += sum_j V[j][v] P[i][j]; B operand slots
-    // 0..3 hold j-tile ga's rows 4g..4g+3, slots 4..7 j-tile gb's (or zero).
-    // The V^T fragments and the first half of the state-update fragments are
-    // published, then the second half is issued.
-    lds_wait();
-#pragma unroll
-    for (int q = 0; q < T::ng; ++q)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) pin(av[q][nt]);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        pin(ka[0][i]);
-        pin(vh[0][i]);
-        pin(vl[0][i]);
-    }
-    kv_frags(1);
-#pragma unroll
-    for (int q = 0; q < T::ng; ++q) {
-        const int ta = T::ga[q], tb = T::gb[q];
-        const int it = T::git[q];
-        const u16x8 bh = cat(p_hi[ta], tb >= 0 ? p_hi[tb] : z4);
-        const u16x8 bl = cat(p_lo[ta], tb >= 0 ? p_lo[tb] : z4);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            part[it][nt] = mma(av[q][nt], bh, part[it][nt]);
-            part[it][nt] = mma(av[q][nt], bl, part[it][nt]);
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // stage 7: state update of rows 32W..32W+31:
-    // S[k][v] = e^{-l c} S + sum_j K[j][k] Vd[j][v]
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) S[mt][nt] *= dc;
+    __builtin_amdgcn_sched_barrier(0);
     lds_wait();
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        pin(ka[1][i]);
-        pin(vh[1][i]);
-        pin(vl[1][i]);
-    }
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            pin(ka[s2][i]);
+            pin(vh[s2][i]);
+            pin(vl[s2][i]);
+        }
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -362,6 +289,79 @@ __device__ __forceinline__ void chunk_compute(const uint16_t *sq, const uint16_t
                 S[mt][nt] = mma(ka[s2][mt], vh[s2][nt], S[mt][nt]);
                 S[mt][nt] = mma(ka[s2][mt], vl[s2][nt], S[mt][nt]);
             }
+}
+
+// One chunk for score wave W: its score tiles (A^T[j][i] = k_j . q_i), weighted
+// and masked by mdec and split hi + lo, times V^T: ipart[q][nt] is the intra
+// term of i-tile Tiles<W>::git[q], column tile nt.  B operand slots 0..3 hold
+// j-tile ga's rows 4g..4g+3, slots 4..7 j-tile gb's (or zero).
+template <int W, bool kF>
+__device__ __forceinline__ void score_chunk(const uint16_t *sq, const uint16_t *sk, const uint16_t *sv,
+                                            const float (&mdec)[12], int g, int l16, f32x4 (&ipart)[2][2]) {
+    using T = Tiles<W>;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const u16x4 z4 = {0, 0, 0, 0};
+
+    u16x8 kf[2][4], qf[2][4];
+#pragma unroll
+    for (int a = 0; a < T::nj; ++a)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kf[a][s] = lds8(&sk[qk_off(16 * T::jl[a] + l16, 32 * s + 8 * g)]);
+#pragma unroll
+    for (int b = 0; b < T::ni; ++b)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qf[b][s] = lds8(&sq[qk_off(16 * T::il[b] + l16, 32 * s + 8 * g)]);
+    u16x8 av[2][2];
+#pragma unroll
+    for (int q = 0; q < T::ng; ++q) {
+        const int ta = T::ga[q], tb = T::gb[q];
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+            av[q][nt] = cat(ldtr_v(sv, 16 * T::jl[T::tj[ta]], 16 * nt, g, l16),
+                            tb >= 0 ? ldtr_v(sv, 16 * T::jl[T::tj[tb]], 16 * nt, g, l16) : z4);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 sc[3];
+#pragma unroll
+    for (int t = 0; t < T::n; ++t) sc[t] = z;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int t = 0; t < T::n; ++t) sc[t] = mma(kf[T::tj[t]][s], qf[T::ti[t]][s], sc[t]);
+    u16x4 p_hi[3], p_lo[3];
+#pragma unroll
+    for (int t = 0; t < T::n; ++t) {
+        f32x4 p;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = sc[t][r] * mdec[4 * t + r];
+        split4(p, p_hi[t], p_lo[t]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    lds_wait();
+#pragma unroll
+    for (int q = 0; q < T::ng; ++q)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) pin(av[q][nt]);
+#pragma unroll
+    for (int q = 0; q < T::ng; ++q) {
+        const int ta = T::ga[q], tb = T::gb[q];
+        const u16x8 bh = cat(p_hi[ta], tb >= 0 ? p_hi[tb] : z4);
+        const u16x8 bl = cat(p_lo[ta], tb >= 0 ? p_lo[tb] : z4);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+            ipart[q][nt] = mma(av[q][nt], bh, z);
+            ipart[q][nt] = mma(av[q][nt], bl, ipart[q][nt]);
+        }
+    }
+}
+
+// Score-wave partials of row block B, added to o.
+template <int B, int W>
+__device__ __forceinline__ void add_intra(const Smem &sm, int nt, int lane, f32x4 &o) {
+    using T = Tiles<W>;
+#pragma unroll
+    for (int q = 0; q < T::ng; ++q)
+        if (T::git[q] == B) o += sm.intra[W][q][nt][lane];
 }
 
 // per-lane weights of wave W's score tiles: element (t, r) is
@@ -401,9 +401,12 @@ struct Job {
     float lam;
 };
 
-// Whole request for wave W of the workgroup.
+// One pass over a request for wave W of the workgroup (0..3 state waves,
+// 4..7 score waves).  Both roles meet the same barriers: two per chunk.
 template <int W, bool kF>
 __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
+    constexpr bool kState = W < 4;
+    constexpr int R = W & 3;  // index within the role
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int l16 = lane & 15, g = lane >> 4;
@@ -415,40 +418,48 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
     const int64_t len = jb.len;
     const int nchunks = static_cast<int>((len + C - 1) / C);
     const int c_last = static_cast<int>(len - static_cast<int64_t>(nchunks - 1) * C);
-
-    float mdec[12], mdec_last[12], qdec[4];
-    score_weights<W, kF>(lam, g, l16, C, mdec);
-    score_weights<W, kF>(lam, g, l16, c_last, mdec_last);
-#pragma unroll
-    for (int it = 0; it < 4; ++it) qdec[it] = expf(-lam * static_cast<float>(16 * it + l16 + 1));
-    // output factor of row block W (token i = 16W + l16)
-    const float fin = kF ? scale * expf(-lam * static_cast<float>(16 * W + l16 - 31)) : scale;
     // state frame: S_m = sigma * S
     const float sigma = kF ? expf(-32.f * lam) : 1.f;
     const float vshift = kF ? 32.f : 0.f;
 
-    // state rows 32W..32W+31 of the block: tile (mt, nt), element r is
-    // S[32W + 16mt + 4g + r][col0 + 16nt + l16]
+    // ---- state role: rows 32R..32R+31 of the block, tile (mt, nt) element r
+    // is S[32R + 16mt + 4g + r][col0 + 16nt + l16]
     f32x4 S[2][2];
+    float qdec[4];
+    float fin = 0.f;
+    const float dc_full = expf(-lam * static_cast<float>(C));
+    const float dc_last = expf(-lam * static_cast<float>(c_last));
+    if constexpr (kState) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                S[mt][nt][r] = sigma * jb.state_in[(32 * W + 16 * mt + 4 * g + r) * D + col0 + 16 * nt + l16];
+                for (int r = 0; r < 4; ++r)
+                    S[mt][nt][r] =
+                        sigma * jb.state_in[(32 * R + 16 * mt + 4 * g + r) * D + col0 + 16 * nt + l16];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) qdec[it] = expf(-lam * static_cast<float>(16 * it + l16 + 1));
+        // output factor of row block R (token i = 16R + l16)
+        fin = kF ? scale * expf(-lam * static_cast<float>(16 * R + l16 - 31)) : scale;
+    }
+    const uint32_t offo = 2u * (static_cast<uint32_t>(16 * R + l16) * row + 4 * g);
 
-    // Async staging.  Wave W copies Q/K rows 16W..16W+15 (4 instructions of
-    // 4 rows each) and V rows 16W..16W+15 (one instruction); lane L of a copy
-    // fills LDS unit L of its 1 KB block, so it loads the logical unit that
-    // the swizzle places there.
+    // ---- score role
+    float mdec[12];
+    if constexpr (!kState) score_weights<R, kF>(lam, g, l16, nchunks == 1 ? c_last : C, mdec);
+
+    // Async staging by the score waves.  Score wave R copies Q/K rows
+    // 16R..16R+15 (4 instructions of 4 rows each) and V rows 16R..16R+15 (one
+    // instruction); lane L of a copy fills LDS unit L of its 1 KB block, so it
+    // loads the logical unit that the swizzle places there.
     int qk_row[4], qk_unit[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        qk_row[u] = 16 * W + 4 * u + (lane >> 4);
+        qk_row[u] = 16 * R + 4 * u + (lane >> 4);
         qk_unit[u] = (lane & 15) ^ swz(qk_row[u]);
     }
-    const int v_row = 16 * W + (lane >> 2);
+    const int v_row = 16 * R + (lane >> 2);
     const int v_unit = (lane & 3) ^ swv(v_row);
     const uint32_t kvrow = static_cast<uint32_t>(jb.kvrow);
     auto issue_copies = [&](int64_t t, int c, int buf) {
@@ -458,26 +469,24 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const uint32_t r = static_cast<uint32_t>(qk_row[u] < c ? qk_row[u] : c - 1);
-            const int dst = (16 * W + 4 * u) * D;
+            const int dst = (16 * R + 4 * u) * D;
             __builtin_amdgcn_global_load_lds(qb + (r * row + 8 * qk_unit[u]), (lds_void *)&sm.q[buf][dst], 16,
                                              0, 0);
             __builtin_amdgcn_global_load_lds(kb + (r * kvrow + 8 * qk_unit[u]), (lds_void *)&sm.k[buf][dst],
                                              16, 0, 0);
         }
         const uint32_t r = static_cast<uint32_t>(v_row < c ? v_row : c - 1);
-        __builtin_amdgcn_global_load_lds(vb + (r * kvrow + 8 * v_unit), (lds_void *)&sm.v[buf][16 * W * VB], 16,
+        __builtin_amdgcn_global_load_lds(vb + (r * kvrow + 8 * v_unit), (lds_void *)&sm.v[buf][16 * R * VB], 16,
                                          0, 0);
     };
 
-    // Decayed V of a staged chunk: thread tid converts V row tid/4, logical
-    // unit tid%4 (8 values) into hi/lo at the same (swizzled) position.
-    const int dv_row = tid >> 2;
+    // Decayed V of a staged chunk: score thread u = tid - 256 converts V row
+    // u/4, logical unit u%4 (8 values) into hi/lo at the same (swizzled) position.
+    const int dv_row = (tid & 255) >> 2;
     const int dv_pos = v_off(dv_row, 8 * (tid & 3));
     // weight of that row in a full chunk and in the last one (zero past its end)
     const float vdec_full = expf(-lam * (static_cast<float>(C - 1 - dv_row) + vshift));
     const float vdec_last = dv_row < c_last ? expf(-lam * (static_cast<float>(c_last - 1 - dv_row) + vshift)) : 0.f;
-    const float dc_full = expf(-lam * static_cast<float>(C));
-    const float dc_last = expf(-lam * static_cast<float>(c_last));
     auto decay_v = [&](int buf, float vdec) {
         const u16x8 pv = lds8(&sm.v[buf][dv_pos]);
         f32x4 x0, x1;
@@ -493,24 +502,24 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
         *reinterpret_cast<u16x8 *>(&sm.vd_lo[dv_pos]) = cat(l0, l1);
     };
 
-    const uint32_t offo = 2u * (static_cast<uint32_t>(16 * W + l16) * row + 4 * g);
-
-    // Every call of issue_copies is 9 vector-memory instructions per wave.
-    // Before publishing chunk ci+1 a wave waits until only the copies of chunk
-    // ci+2 (issued later, in program order) may still be outstanding.
+    // Every call of issue_copies is 9 vector-memory instructions per score wave.
+    // Before publishing chunk ci+1 a score wave waits until only the copies of
+    // chunk ci+2 (issued later, in program order) may still be outstanding.
     auto wait_all = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
     auto wait_all_but_one_chunk = [] { asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); };
 
     // prologue: chunks 0 and 1 in flight, chunk 0 published and decayed
-    issue_copies(jb.t0, nchunks == 1 ? c_last : C, 0);
-    if (nchunks > 1) {
-        issue_copies(jb.t0 + C, nchunks == 2 ? c_last : C, 1);
-        wait_all_but_one_chunk();
-    } else {
-        wait_all();
+    if constexpr (!kState) {
+        issue_copies(jb.t0, nchunks == 1 ? c_last : C, 0);
+        if (nchunks > 1) {
+            issue_copies(jb.t0 + C, nchunks == 2 ? c_last : C, 1);
+            wait_all_but_one_chunk();
+        } else {
+            wait_all();
+        }
     }
     __syncthreads();
-    decay_v(0, nchunks == 1 ? vdec_last : vdec_full);
+    if constexpr (!kState) decay_v(0, nchunks == 1 ? vdec_last : vdec_full);
 
     int buf = 0;  // ring slot of chunk ci
     for (int ci = 0; ci < nchunks; ++ci) {
@@ -521,59 +530,71 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
         const int nnbuf = nbuf == NBUF - 1 ? 0 : nbuf + 1;    // slot of chunk ci+2
         lds_barrier();  // chunk ci staged and decayed; previous partials consumed
 
-        const bool ahead = ci + 2 < nchunks;
-        if (ahead) issue_copies(t + 2 * C, ci + 3 == nchunks ? c_last : C, nnbuf);
+        if constexpr (kState) {
+            f32x4 part[4][2];
+            state_chunk<R, kF>(sm.q[buf], sm.k[buf], sm.vd_hi, sm.vd_lo, qdec, last ? dc_last : dc_full, g,
+                               l16, S, part);
+            // hand the inter partials of the other row blocks to their state waves
+#pragma unroll
+            for (int it = 0; it < 4; ++it)
+                if (it != R)
+#pragma unroll
+                    for (int nt = 0; nt < 2; ++nt) sm.inter[R][it < R ? it : it - 1][nt][lane] = part[it][nt];
+            lds_barrier();  // every partial of the chunk is in LDS
 
-        f32x4 part[4][2];
-        if (!last)
-            chunk_compute<W, kF>(sm.q[buf], sm.k[buf], sm.v[buf], sm.vd_hi, sm.vd_lo, mdec, qdec, dc_full,
-                                 g, l16, S, part);
-        else
-            chunk_compute<W, kF>(sm.q[buf], sm.k[buf], sm.v[buf], sm.vd_hi, sm.vd_lo, mdec_last, qdec,
-                                 dc_last, g, l16, S, part);
-
-        // hand the partial O^T tiles of the other row blocks to their owners
+            // row block R: sum the partials and store o.
+            // O^T tile nt, element r: value column col0 + 16nt + 4g + r, token 16R + l16
+            char *ob = reinterpret_cast<char *>(jb.out + t * jb.row + jb.hcol + col0);
+            const bool store = !last || (16 * R + l16) < c;
 #pragma unroll
-        for (int it = 0; it < 4; ++it)
-            if (it != W)
+            for (int nt = 0; nt < 2; ++nt) {
+                f32x4 o = part[R][nt];
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) sm.part[W][it][nt][lane] = part[it][nt];
-        if (ahead)
-            wait_all_but_one_chunk();  // this wave's copies of chunk ci+1 landed
-        else
-            wait_all();
-        lds_barrier();
-
-        // row block W: sum the four partials and store o.
-        // O^T tile nt, element r: value column col0 + 16nt + 4g + r, token 16W + l16
-        char *ob = reinterpret_cast<char *>(jb.out + t * jb.row + jb.hcol + col0);
-        const bool store = !last || (16 * W + l16) < c;
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            f32x4 o = part[W][nt];
-#pragma unroll
-            for (int src = 0; src < 4; ++src)
-                if (src != W) o += sm.part[src][W][nt][lane];
-            if (store) {
-                o *= fin;
-                const uint64_t packed = (uint64_t)cvt2(o[0], o[1]) | ((uint64_t)cvt2(o[2], o[3]) << 32);
-                *reinterpret_cast<uint64_t *>(ob + offo + 32 * nt) = packed;
+                for (int s = 0; s < 4; ++s)
+                    if (s != R) o += sm.inter[s][R < s ? R : R - 1][nt][lane];
+                add_intra<R, 0>(sm, nt, lane, o);
+                add_intra<R, 1>(sm, nt, lane, o);
+                add_intra<R, 2>(sm, nt, lane, o);
+                add_intra<R, 3>(sm, nt, lane, o);
+                if (store) {
+                    o *= fin;
+                    const uint64_t packed = (uint64_t)cvt2(o[0], o[1]) | ((uint64_t)cvt2(o[2], o[3]) << 32);
+                    *reinterpret_cast<uint64_t *>(ob + offo + 32 * nt) = packed;
+                }
             }
+        } else {
+            const bool ahead = ci + 2 < nchunks;
+            if (ahead) issue_copies(t + 2 * C, ci + 3 == nchunks ? c_last : C, nnbuf);
+            if (last && c_last != C && nchunks > 1) score_weights<R, kF>(lam, g, l16, c_last, mdec);
+            f32x4 ipart[2][2];
+            score_chunk<R, kF>(sm.q[buf], sm.k[buf], sm.v[buf], mdec, g, l16, ipart);
+#pragma unroll
+            for (int q = 0; q < Tiles<R>::ng; ++q)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) sm.intra[R][q][nt][lane] = ipart[q][nt];
+            if (ahead)
+                wait_all_but_one_chunk();  // this wave's copies of chunk ci+1 landed
+            else
+                wait_all();
+            lds_barrier();  // every partial of the chunk is in LDS; chunk ci+1 staged
+            // decayed V of the next chunk (its copies are visible after the barrier
+            // above, and the state waves' update of this chunk no longer reads vd)
+            if (!last) decay_v(nbuf, ci + 2 == nchunks ? vdec_last : vdec_full);
         }
-        // decayed V of the next chunk (its copies are visible after the barrier
-        // above, and this chunk's state update no longer reads vd)
-        if (!last) decay_v(nbuf, ci + 2 == nchunks ? vdec_last : vdec_full);
         buf = nbuf;
     }
 
-    const float unscale = kF ? expf(32.f * lam) : 1.f;
+    if constexpr (kState) {
+        const float unscale = kF ? expf(32.f * lam) : 1.f;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+            for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                jb.state_out[(32 * W + 16 * mt + 4 * g + r) * D + col0 + 16 * nt + l16] = S[mt][nt][r] * unscale;
+                for (int r = 0; r < 4; ++r)
+                    jb.state_out[(32 * R + 16 * mt + 4 * g + r) * D + col0 + 16 * nt + l16] =
+                        S[mt][nt][r] * unscale;
+    }
 }
 
 // The passes of wave W over a request: one over [0, len), or with a snapshot
@@ -649,15 +670,23 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(PrefillArgs a) {
     // slopes in [0, 2] take the factored decay path (the largest ALiBi slope
     // is below 1); anything else the explicit one
     const bool factored = base.lam >= 0.f && base.lam <= 2.f;
-    switch (__builtin_amdgcn_readfirstlane(tid >> 6) + (factored ? 0 : 4)) {
+    switch (__builtin_amdgcn_readfirstlane(tid >> 6) + (factored ? 0 : 8)) {
     case 0: run_passes<0, true>(sm, base, split, tl); break;
     case 1: run_passes<1, true>(sm, base, split, tl); break;
     case 2: run_passes<2, true>(sm, base, split, tl); break;
     case 3: run_passes<3, true>(sm, base, split, tl); break;
-    case 4: run_passes<0, false>(sm, base, split, tl); break;
-    case 5: run_passes<1, false>(sm, base, split, tl); break;
-    case 6: run_passes<2, false>(sm, base, split, tl); break;
-    default: run_passes<3, false>(sm, base, split, tl); break;
+    case 4: run_passes<4, true>(sm, base, split, tl); break;
+    case 5: run_passes<5, true>(sm, base, split, tl); break;
+    case 6: run_passes<6, true>(sm, base, split, tl); break;
+    case 7: run_passes<7, true>(sm, base, split, tl); break;
+    case 8: run_passes<0, false>(sm, base, split, tl); break;
+    case 9: run_passes<1, false>(sm, base, split, tl); break;
+    case 10: run_passes<2, false>(sm, base, split, tl); break;
+    case 11: run_passes<3, false>(sm, base, split, tl); break;
+    case 12: run_passes<4, false>(sm, base, split, tl); break;
+    case 13: run_passes<5, false>(sm, base, split, tl); break;
+    case 14: run_passes<6, false>(sm, base, split, tl); break;
+    default: run_passes<7, false>(sm, base, split, tl); break;
     }
     if (track && tl == len) {
         // snapshot after the whole request: the final state, as stored above
