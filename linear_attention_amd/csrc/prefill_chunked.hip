@@ -38,10 +38,12 @@
 // Data movement.  Q, K and V tiles are copied from global memory straight
 // into a 3-deep LDS staging ring (global_load_lds_dwordx4: lane L of a wave
 // writes 16 bytes at base + 16 L), two chunks ahead of the chunk being
-// computed, so staging costs no registers and a chunk's loads have two chunk
-// times to arrive.  Each wave waits only for its own copies of the next chunk
-// (a counted vmcnt that leaves the newest chunk's copies in flight) before the
-// barrier that publishes them.  Operands
+// computed, so staging costs no registers.  A wave's copies do not complete in
+// issue order, so a counted vmcnt that leaves the newest chunk's copies in
+// flight does not prove that the older chunk has landed (measured: stale tiles
+// under load).  Before the barrier that publishes chunk ci+1 each copying wave
+// therefore waits for all of its copies (vmcnt(0)), those of chunk ci+2
+// included.  Operands
 // that the MFMA needs with tokens along the contraction (K^T, V^T, Vd) are
 // read from the token-major tiles with ds_read_b64_tr_b16, whose 16-lane
 // groups return the columns of a 4-row block.  Tile rows are XOR-swizzled in
@@ -380,9 +382,10 @@ __device__ __forceinline__ void score_weights(float lam, int g, int l16, int c, 
         }
 }
 
-// Workgroup barrier for LDS data only.  __syncthreads() would also wait for
-// every outstanding global->LDS copy (it is a release fence); the copies are
-// waited for explicitly with counted vmcnt waits instead.
+// Workgroup barrier for LDS data only.  __syncthreads() would also make every
+// wave wait for all of its outstanding global->LDS copies (it is a release
+// fence); the copying waves wait for theirs explicitly before the barriers
+// that publish a chunk.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -502,21 +505,15 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
         *reinterpret_cast<u16x8 *>(&sm.vd_lo[dv_pos]) = cat(l0, l1);
     };
 
-    // Every call of issue_copies is 9 vector-memory instructions per score wave.
-    // Before publishing chunk ci+1 a score wave waits until only the copies of
-    // chunk ci+2 (issued later, in program order) may still be outstanding.
+    // Copies of one wave can complete out of issue order, so only vmcnt(0)
+    // proves that a chunk has landed.
     auto wait_all = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
-    auto wait_all_but_one_chunk = [] { asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); };
 
     // prologue: chunks 0 and 1 in flight, chunk 0 published and decayed
     if constexpr (!kState) {
         issue_copies(jb.t0, nchunks == 1 ? c_last : C, 0);
-        if (nchunks > 1) {
-            issue_copies(jb.t0 + C, nchunks == 2 ? c_last : C, 1);
-            wait_all_but_one_chunk();
-        } else {
-            wait_all();
-        }
+        if (nchunks > 1) issue_copies(jb.t0 + C, nchunks == 2 ? c_last : C, 1);
+        wait_all();
     }
     __syncthreads();
     if constexpr (!kState) decay_v(0, nchunks == 1 ? vdec_last : vdec_full);
@@ -572,10 +569,7 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
             for (int q = 0; q < Tiles<R>::ng; ++q)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) sm.intra[R][q][nt][lane] = ipart[q][nt];
-            if (ahead)
-                wait_all_but_one_chunk();  // this wave's copies of chunk ci+1 landed
-            else
-                wait_all();
+            wait_all();     // this wave's copies of chunks ci+1 (and ci+2) landed
             lds_barrier();  // every partial of the chunk is in LDS; chunk ci+1 staged
             // decayed V of the next chunk (its copies are visible after the barrier
             // above, and the state waves' update of this chunk no longer reads vd)
