@@ -30,20 +30,23 @@
 //     term of all 64 tokens restricted to its rows (no state exchange) and the
 //     update of its rows, and it sums and stores the output of row block s;
 //   * score wave w (0..3) computes a balanced share of the 10 causal score
-//     tiles and their P V products, stages a quarter of every chunk, and
-//     decays a quarter of the next chunk's V.
+//     tiles and their P V products, and decays a quarter of the next chunk's V;
+// both roles stage chunks, in turn (see Data movement).
 // The partial O^T tiles meet in LDS, where the state wave of each 16-token row
 // block adds them up.
 //
-// Data movement.  Q, K and V tiles are copied from global memory straight
-// into a 3-deep LDS staging ring (global_load_lds_dwordx4: lane L of a wave
-// writes 16 bytes at base + 16 L), two chunks ahead of the chunk being
-// computed, so staging costs no registers.  A wave's copies do not complete in
-// issue order, so a counted vmcnt that leaves the newest chunk's copies in
-// flight does not prove that the older chunk has landed (measured: stale tiles
-// under load).  Before the barrier that publishes chunk ci+1 each copying wave
-// therefore waits for all of its copies (vmcnt(0)), those of chunk ci+2
-// included.  Operands
+// Data movement.  Global loads take about two microseconds under this load,
+// so the tiles of two chunks are kept in flight.  The two roles stage the
+// chunks in turn (score waves the even ones, state waves the odd ones): at
+// the start of chunk i the role that staged chunk i+1 writes it from its
+// registers to a 2-slot LDS ring, where the barrier in the middle of chunk i
+// publishes it, and then loads chunk i+3 into the same registers, two chunk
+// times before they are written.  Each wave has at most one chunk of loads in
+// flight, so vmcnt(0) before the write waits for exactly that chunk.  (Copying
+// global memory straight into LDS was slower once made safe: those copies do
+// not complete in issue order, and copies left in flight across a barrier gave
+// stale tiles under load.)
+// Operands
 // that the MFMA needs with tokens along the contraction (K^T, V^T, Vd) are
 // read from the token-major tiles with ds_read_b64_tr_b16, whose 16-lane
 // groups return the columns of a 4-row block.  Tile rows are XOR-swizzled in
@@ -75,14 +78,23 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Q and K tiles: 64 rows of 128 elements (256 B, one pass over the 64 LDS
-// banks); the 16-byte units of row r are permuted by u -> u ^ swz(r).  swz
-// takes 16 distinct values over any 16 consecutive rows (16-byte reads of one
-// column unit from 16 rows hit distinct banks) and maps the unit pair
-// {2m, 2m+1} of 4 consecutive rows to 4 distinct pairs (the 4x16 transposed
-// reads hit distinct banks).
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-__device__ __forceinline__ int qk_off(int r, int col) {
-    return r * D + ((((col >> 3) ^ swz(r)) << 3) | (col & 7));
+// banks); the 16-byte units of row r are permuted by u -> u ^ m(r), with a
+// mask per tile chosen for the reads that tile serves, each measured free of
+// bank conflicts on gfx950 (LDS conflict counters on a microbenchmark of
+// every access pattern):
+//   Q: 16-byte score-fragment reads and 8-byte inter-term reads -> m(r) = r
+//   K: 16-byte score-fragment reads and 4x16 transposed reads
+//      -> m(r) = ((r & 7) << 1) | (r & 1)
+// (No single mask serves both tiles: the 16-byte reads want rows r and r + 8
+// to share a mask, the 8-byte reads want them apart, and the transposed reads
+// want bits 1..3 of the mask to differ within every 8 rows.)
+__device__ __forceinline__ int swz_q(int r) { return r & 15; }
+__device__ __forceinline__ int swz_k(int r) { return ((r & 7) << 1) | (r & 1); }
+__device__ __forceinline__ int q_off(int r, int col) {
+    return r * D + ((((col >> 3) ^ swz_q(r)) << 3) | (col & 7));
+}
+__device__ __forceinline__ int k_off(int r, int col) {
+    return r * D + ((((col >> 3) ^ swz_k(r)) << 3) | (col & 7));
 }
 // V tiles: 64 rows of 32 elements (64 B); units permuted by u -> u ^ swv(r),
 // which moves rows 4..7 of every 8 to the other half of the banks.
@@ -91,10 +103,10 @@ __device__ __forceinline__ int v_off(int r, int col) {
     return r * VB + ((((col >> 3) ^ swv(r)) << 3) | (col & 7));
 }
 
-constexpr int NBUF = 3;  // staging buffers: copies run two chunks ahead
+constexpr int NBUF = 2;  // LDS slots: the chunk being computed and the next
 
 struct Smem {
-    uint16_t q[NBUF][C * D];  // staging ring
+    uint16_t q[NBUF][C * D];  // tile ring
     uint16_t k[NBUF][C * D];
     uint16_t v[NBUF][C * VB];
     uint16_t vd_hi[C * VB];   // decayed V of the current chunk, hi/lo
@@ -132,8 +144,8 @@ __device__ __forceinline__ u16x4 tr_at(const uint16_t *p) {
 }
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void pin(u16x8 &x) { asm volatile("" : "+v"(x)); }
-__device__ __forceinline__ u16x4 ldtr_qk(const uint16_t *tile, int row0, int col0, int g, int l16) {
-    return tr_at(tile + qk_off(row0 + 4 * g + (l16 >> 2), col0 + 4 * (l16 & 3)));
+__device__ __forceinline__ u16x4 ldtr_k(const uint16_t *tile, int row0, int col0, int g, int l16) {
+    return tr_at(tile + k_off(row0 + 4 * g + (l16 >> 2), col0 + 4 * (l16 & 3)));
 }
 __device__ __forceinline__ u16x4 ldtr_v(const uint16_t *tile, int row0, int col0, int g, int l16) {
     return tr_at(tile + v_off(row0 + 4 * g + (l16 >> 2), col0 + 4 * (l16 & 3)));
@@ -229,7 +241,7 @@ __device__ __forceinline__ void state_chunk(const uint16_t *sq, const uint16_t *
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int qr = 16 * it + l16;
-        qb[it] = cat(lds4(&sq[qk_off(qr, 32 * SW + 4 * g)]), lds4(&sq[qk_off(qr, 32 * SW + 16 + 4 * g)]));
+        qb[it] = cat(lds4(&sq[q_off(qr, 32 * SW + 4 * g)]), lds4(&sq[q_off(qr, 32 * SW + 16 + 4 * g)]));
     }
     // the state as bf16 hi/lo A operand (v x k): lane (g, l16) holds rows
     // k = 32SW + 4g + r (mt 0) and 32SW + 16 + 4g + r (mt 1) of column v = l16
@@ -260,8 +272,8 @@ __device__ __forceinline__ void state_chunk(const uint16_t *sq, const uint16_t *
     for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
-            ka[s2][mt] = cat(ldtr_qk(sk, 32 * s2, 32 * SW + 16 * mt, g, l16),
-                             ldtr_qk(sk, 32 * s2 + 16, 32 * SW + 16 * mt, g, l16));
+            ka[s2][mt] = cat(ldtr_k(sk, 32 * s2, 32 * SW + 16 * mt, g, l16),
+                             ldtr_k(sk, 32 * s2 + 16, 32 * SW + 16 * mt, g, l16));
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             vh[s2][nt] = cat(ldtr_v(svh, 32 * s2, 16 * nt, g, l16), ldtr_v(svh, 32 * s2 + 16, 16 * nt, g, l16));
@@ -308,11 +320,11 @@ __device__ __forceinline__ void score_chunk(const uint16_t *sq, const uint16_t *
 #pragma unroll
     for (int a = 0; a < T::nj; ++a)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) kf[a][s] = lds8(&sk[qk_off(16 * T::jl[a] + l16, 32 * s + 8 * g)]);
+        for (int s = 0; s < 4; ++s) kf[a][s] = lds8(&sk[k_off(16 * T::jl[a] + l16, 32 * s + 8 * g)]);
 #pragma unroll
     for (int b = 0; b < T::ni; ++b)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) qf[b][s] = lds8(&sq[qk_off(16 * T::il[b] + l16, 32 * s + 8 * g)]);
+        for (int s = 0; s < 4; ++s) qf[b][s] = lds8(&sq[q_off(16 * T::il[b] + l16, 32 * s + 8 * g)]);
     u16x8 av[2][2];
 #pragma unroll
     for (int q = 0; q < T::ng; ++q) {
@@ -383,9 +395,8 @@ __device__ __forceinline__ void score_weights(float lam, int g, int l16, int c, 
 }
 
 // Workgroup barrier for LDS data only.  __syncthreads() would also make every
-// wave wait for all of its outstanding global->LDS copies (it is a release
-// fence); the copying waves wait for theirs explicitly before the barriers
-// that publish a chunk.
+// wave wait for its outstanding global loads (it is a release fence), which
+// would drain the score waves' loads of the chunk after next.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -452,35 +463,43 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
     float mdec[12];
     if constexpr (!kState) score_weights<R, kF>(lam, g, l16, nchunks == 1 ? c_last : C, mdec);
 
-    // Async staging by the score waves.  Score wave R copies Q/K rows
-    // 16R..16R+15 (4 instructions of 4 rows each) and V rows 16R..16R+15 (one
-    // instruction); lane L of a copy fills LDS unit L of its 1 KB block, so it
-    // loads the logical unit that the swizzle places there.
-    int qk_row[4], qk_unit[4];
+    // Staging.  Wave R of the staging role moves Q/K rows 16R..16R+15 (4
+    // blocks of 4 rows) and V rows 16R..16R+15 (one block): lane L holds unit L
+    // of each 1 KB block, so it loads the logical unit that the swizzle places
+    // there.  Rows past the end of a short chunk repeat its last row.
+    int qk_row[4], q_unit[4], k_unit[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         qk_row[u] = 16 * R + 4 * u + (lane >> 4);
-        qk_unit[u] = (lane & 15) ^ swz(qk_row[u]);
+        q_unit[u] = (lane & 15) ^ swz_q(qk_row[u]);
+        k_unit[u] = (lane & 15) ^ swz_k(qk_row[u]);
     }
     const int v_row = 16 * R + (lane >> 2);
     const int v_unit = (lane & 3) ^ swv(v_row);
     const uint32_t kvrow = static_cast<uint32_t>(jb.kvrow);
-    auto issue_copies = [&](int64_t t, int c, int buf) {
+    u16x8 rq[4], rk[4], rv;  // the chunk in flight
+    auto load_chunk = [&](int64_t t, int c) {
         const uint16_t *qb = jb.q + t * jb.row + jb.hcol;
         const uint16_t *kb = jb.k + t * jb.kvrow + jb.kvcol;
         const uint16_t *vb = jb.v + t * jb.kvrow + jb.kvcol + col0;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const uint32_t r = static_cast<uint32_t>(qk_row[u] < c ? qk_row[u] : c - 1);
-            const int dst = (16 * R + 4 * u) * D;
-            __builtin_amdgcn_global_load_lds(qb + (r * row + 8 * qk_unit[u]), (lds_void *)&sm.q[buf][dst], 16,
-                                             0, 0);
-            __builtin_amdgcn_global_load_lds(kb + (r * kvrow + 8 * qk_unit[u]), (lds_void *)&sm.k[buf][dst],
-                                             16, 0, 0);
+            rq[u] = *reinterpret_cast<const u16x8 *>(qb + (r * row + 8 * q_unit[u]));
+            rk[u] = *reinterpret_cast<const u16x8 *>(kb + (r * kvrow + 8 * k_unit[u]));
         }
         const uint32_t r = static_cast<uint32_t>(v_row < c ? v_row : c - 1);
-        __builtin_amdgcn_global_load_lds(vb + (r * kvrow + 8 * v_unit), (lds_void *)&sm.v[buf][16 * R * VB], 16,
-                                         0, 0);
+        rv = *reinterpret_cast<const u16x8 *>(vb + (r * kvrow + 8 * v_unit));
+    };
+    auto store_chunk = [&](int buf) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the loads of the chunk landed
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int dst = (16 * R + 4 * u) * D + 8 * lane;
+            *reinterpret_cast<u16x8 *>(&sm.q[buf][dst]) = rq[u];
+            *reinterpret_cast<u16x8 *>(&sm.k[buf][dst]) = rk[u];
+        }
+        *reinterpret_cast<u16x8 *>(&sm.v[buf][16 * R * VB + 8 * lane]) = rv;
     };
 
     // Decayed V of a staged chunk: score thread u = tid - 256 converts V row
@@ -505,16 +524,19 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
         *reinterpret_cast<u16x8 *>(&sm.vd_lo[dv_pos]) = cat(l0, l1);
     };
 
-    // Copies of one wave can complete out of issue order, so only vmcnt(0)
-    // proves that a chunk has landed.
-    auto wait_all = [] { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+    // chunk n is staged by the score waves when n is even, by the state waves
+    // when n is odd
+    auto stages = [](int n) { return ((n & 1) != 0) == kState; };
+    auto chunk_t = [&](int n) { return jb.t0 + static_cast<int64_t>(n) * C; };
+    auto chunk_c = [&](int n) { return n + 1 == nchunks ? c_last : C; };
 
-    // prologue: chunks 0 and 1 in flight, chunk 0 published and decayed
-    if constexpr (!kState) {
-        issue_copies(jb.t0, nchunks == 1 ? c_last : C, 0);
-        if (nchunks > 1) issue_copies(jb.t0 + C, nchunks == 2 ? c_last : C, 1);
-        wait_all();
+    // prologue: chunk 0 in LDS, published and decayed; chunks 1 and 2 in flight
+    if (stages(0)) {
+        load_chunk(chunk_t(0), chunk_c(0));
+        store_chunk(0);
     }
+    for (int n = 1; n <= 2; ++n)
+        if (n < nchunks && stages(n)) load_chunk(chunk_t(n), chunk_c(n));
     __syncthreads();
     if constexpr (!kState) decay_v(0, nchunks == 1 ? vdec_last : vdec_full);
 
@@ -523,9 +545,14 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
         const int64_t t = jb.t0 + static_cast<int64_t>(ci) * C;
         const bool last = ci + 1 == nchunks;
         const int c = last ? c_last : C;
-        const int nbuf = buf == NBUF - 1 ? 0 : buf + 1;       // slot of chunk ci+1
-        const int nnbuf = nbuf == NBUF - 1 ? 0 : nbuf + 1;    // slot of chunk ci+2
+        const int nbuf = buf ^ 1;  // slot of chunk ci+1 (chunk ci-1's, read before the last barrier)
         lds_barrier();  // chunk ci staged and decayed; previous partials consumed
+        // chunk ci+1 from registers to LDS (published at the next barrier), then
+        // chunk ci+3 from global memory to the same registers
+        if (ci + 1 < nchunks && stages(ci + 1)) {
+            store_chunk(nbuf);
+            if (ci + 3 < nchunks) load_chunk(chunk_t(ci + 3), chunk_c(ci + 3));
+        }
 
         if constexpr (kState) {
             f32x4 part[4][2];
@@ -560,8 +587,6 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
                 }
             }
         } else {
-            const bool ahead = ci + 2 < nchunks;
-            if (ahead) issue_copies(t + 2 * C, ci + 3 == nchunks ? c_last : C, nnbuf);
             if (last && c_last != C && nchunks > 1) score_weights<R, kF>(lam, g, l16, c_last, mdec);
             f32x4 ipart[2][2];
             score_chunk<R, kF>(sm.q[buf], sm.k[buf], sm.v[buf], mdec, g, l16, ipart);
@@ -569,10 +594,9 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
             for (int q = 0; q < Tiles<R>::ng; ++q)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) sm.intra[R][q][nt][lane] = ipart[q][nt];
-            wait_all();     // this wave's copies of chunks ci+1 (and ci+2) landed
             lds_barrier();  // every partial of the chunk is in LDS; chunk ci+1 staged
-            // decayed V of the next chunk (its copies are visible after the barrier
-            // above, and the state waves' update of this chunk no longer reads vd)
+            // decayed V of the next chunk (visible after the barrier above; the
+            // state waves' update of this chunk no longer reads vd)
             if (!last) decay_v(nbuf, ci + 2 == nchunks ? vdec_last : vdec_full);
         }
         buf = nbuf;
