@@ -17,6 +17,9 @@ After the timed steps, outside the step time:
   * graph  32 small decode calls (1 request, H=64, one pool per call, as one
            per layer) launched eagerly and as one captured HIP graph: host
            launch overhead per call, eager vs graph
+  * prefill variants on slices of the long-prefill tensors (made on the
+    device): a state-tracking snapshot at token 65536; grouped heads with
+    8 kv heads for the 64 query heads; head_dim 64 over 16384 tokens
 
 Algorithmic traffic (bytes the method must move; bf16 I/O, fp32 state):
   prefill: 1024 B per (token, head) for q, k, v in and o out, plus 128 KiB of
@@ -99,6 +102,28 @@ def step_bytes(B, H, tokens):
 
 def tree_bytes(B, n, H):
     return B * H * STATE_BYTES + B * n * H * STATE_BYTES + B * n * H * 4 * D * 2
+
+
+def prefill_variants(ms, ms_min, T, H):
+    """Rates of the prefill variants timed after the steps."""
+    if "prefill_track" not in ms:
+        return None
+    T64 = 16384
+    gqa_bytes = T * H * (2 * D * 2) + T * 8 * (2 * D * 2) + H * 2 * STATE_BYTES
+    d64_bytes = T64 * H * 4 * 64 * 2 + H * 2 * 64 * 64 * 4
+    return {
+        "track_snapshot": {"workload": f"long prefill T={T} H={H} d={D}, snapshot after {T // 2} tokens",
+                           "avg_ms": ms["prefill_track"], "min_ms": ms_min["prefill_track"],
+                           "tokens_per_s": T / (ms["prefill_track"] * 1e-3),
+                           "vs_untracked": ms["prefill"] / ms["prefill_track"]},
+        "grouped_heads": {"workload": f"prefill T={T} H={H} Hkv=8 d={D}", "avg_ms": ms["prefill_gqa"],
+                          "min_ms": ms_min["prefill_gqa"], "tokens_per_s": T / (ms["prefill_gqa"] * 1e-3),
+                          "hbm_gbs": gqa_bytes / (ms["prefill_gqa"] * 1e-3) / 1e9},
+        "head_dim_64": {"workload": f"prefill T={T64} H={H} d=64 (token-recurrent kernel)",
+                        "avg_ms": ms["prefill_d64"], "min_ms": ms_min["prefill_d64"],
+                        "tokens_per_s": T64 / (ms["prefill_d64"] * 1e-3),
+                        "hbm_gbs": d64_bytes / (ms["prefill_d64"] * 1e-3) / 1e9},
+    }
 
 
 def graph_latency(la, W, np, torch, dev, upload, warmup, reps, layers=32, batch=1):
@@ -237,6 +262,35 @@ def main():
     calls = [(n, f) for n, f in (("prefill", run_prefill), ("decode", run_decode),
                                  ("verify", run_verify)) if n in want]
     extra = [("tree", run_tree)] if "tree" in want else []
+    if "prefill" in want and not args.only:
+        # variants of the long prefill, made from its device tensors
+        T4 = wp.total_tokens
+        V4 = {"track_lens": torch.tensor([T4 // 2], dtype=torch.int32, device=dev),
+              "track_slot": torch.tensor([1], dtype=torch.int32, device=dev),
+              "k8": P["k"][:, :8].contiguous(), "v8": P["v"][:, :8].contiguous(),
+              "out_g": torch.empty_like(P["q"]),
+              "pool_g": torch.zeros((2, 64, D, D), device=dev)}
+        T64 = 16384
+        V4.update({"q64": P["q"][:T64, :, :64].contiguous(), "k64": P["k"][:T64, :, :64].contiguous(),
+                   "v64": P["v"][:T64, :, :64].contiguous(),
+                   "cu64": torch.tensor([0, T64], dtype=torch.int32, device=dev),
+                   "pool64": torch.zeros((2, 64, 64, 64), device=dev)})
+        V4["out64"] = torch.empty_like(V4["q64"])
+
+        def run_track():
+            la.la_prefill(P["q"], P["k"], P["v"], P["cu"], P["pool"], P["slot"], P["slopes"], P["out"],
+                          wp.max_seqlen, track_lens=V4["track_lens"], track_slot_idx=V4["track_slot"],
+                          stream=stream)
+
+        def run_gqa():
+            la.la_prefill(P["q"], V4["k8"], V4["v8"], P["cu"], V4["pool_g"], P["slot"], P["slopes"],
+                          V4["out_g"], wp.max_seqlen, stream=stream)
+
+        def run_d64():
+            la.la_prefill(V4["q64"], V4["k64"], V4["v64"], V4["cu64"], V4["pool64"], P["slot"], P["slopes"],
+                          V4["out64"], T64, stream=stream)
+
+        extra += [("prefill_track", run_track), ("prefill_gqa", run_gqa), ("prefill_d64", run_d64)]
     for _ in range(args.warmup):
         for _, fn in calls + extra:
             fn()
@@ -347,6 +401,7 @@ def main():
                          "kernel": "tree_kernel<bf16>", "algorithmic_bytes": tb},
         },
         "decode_graph": graph,
+        "prefill_variants": prefill_variants(ms, ms_min, wp.total_tokens, H),
         "prefill_min_ms": ms_min["prefill"],
         "cpu_baseline": None,
     }
