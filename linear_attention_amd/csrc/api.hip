@@ -145,7 +145,7 @@ la_status la_prefill(const void *q, const void *k, const void *v, la_dtype dtype
     // with every request empty there is nothing to compute, but a snapshot
     // after 0 tokens still copies the prefix state
     if (batch == 0 || ((max_seqlen == 0 || total_tokens == 0) && !track_lens)) return LA_OK;
-    if (dtype == LA_DTYPE_BF16 && head_dim == la::kHeadDim) {
+    if (dtype == LA_DTYPE_BF16) {
         la::PrefillArgs a{};
         a.q = static_cast<const uint16_t *>(q);
         a.k = static_cast<const uint16_t *>(k);
@@ -161,7 +161,7 @@ la_status la_prefill(const void *q, const void *k, const void *v, la_dtype dtype
         a.track_slot_idx = track_slot_idx;
         a.slopes = slopes;
         a.out = static_cast<uint16_t *>(out);
-        return from_hip(la::launch_prefill_chunked(a, batch, stream));
+        return from_hip(la::launch_prefill_chunked(a, batch, head_dim, stream));
     }
     la::RecurrentArgs a{};
     a.q = q;

@@ -5,7 +5,6 @@
 
 namespace la {
 
-constexpr int kHeadDim = 128;  // head_dim of the chunked MFMA prefill
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

@@ -44,8 +44,8 @@ struct TreeArgs {
 };
 hipError_t launch_tree(const TreeArgs &a, bool bf16, int head_dim, int batch, hipStream_t stream);
 
-// Chunked bf16 MFMA prefill (head_dim 128): one workgroup per (request, head,
-// 32-column block of the state), chunks of 64 tokens.
+// Chunked bf16 MFMA prefill (head_dim 128 or 64): one workgroup per (request,
+// head, 32-column block of the state), chunks of 64 tokens.
 struct PrefillArgs {
     const uint16_t *q, *k, *v;
     const int32_t *cu_seqlens;
@@ -58,6 +58,6 @@ struct PrefillArgs {
     const float *slopes;
     uint16_t *out;
 };
-hipError_t launch_prefill_chunked(const PrefillArgs &a, int batch, hipStream_t stream);
+hipError_t launch_prefill_chunked(const PrefillArgs &a, int batch, int head_dim, hipStream_t stream);
 
 }  // namespace la

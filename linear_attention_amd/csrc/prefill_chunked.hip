@@ -19,19 +19,22 @@
 // an exact bf16 input to ~2^-17 relative error; without it the bf16 rounding
 // of P, S_prev and Vd each add output errors of order 1e-2 on small-slope heads.
 //
-// Work split.  One workgroup of 8 waves (two per SIMD) per (request, head,
-// 32-column block of S); the block id is mapped so the 4 column blocks of a
-// head share an XCD (ids are dealt to the 8 XCDs round-robin) and its L2 serves
-// their repeated Q/K reads.  The waves take two roles, so that each fits in
-// half of a SIMD's registers and the SIMD can overlap one wave's MFMAs with the
-// other's vector and LDS work:
-//   * state wave s (0..3) keeps the fp32 state rows 32s..32s+31 of the block in
-//     MFMA accumulators for the whole request; per chunk it computes the inter
-//     term of all 64 tokens restricted to its rows (no state exchange) and the
-//     update of its rows, and it sums and stores the output of row block s;
-//   * score wave w (0..3) computes a balanced share of the 10 causal score
-//     tiles and their P V products, and decays a quarter of the next chunk's V;
-// both roles stage chunks, in turn (see Data movement).
+// Work split.  One workgroup per (request, head, 32-column block of S); the
+// block id is mapped so the column blocks of a head share an XCD (ids are
+// dealt to the 8 XCDs round-robin) and its L2 serves their repeated Q/K reads.
+// The waves take two roles, so that each fits in half of a SIMD's registers
+// and a SIMD can overlap one wave's MFMAs with another's vector and LDS work:
+//   * state wave s (D/32 of them: 4 for D = 128, 2 for D = 64) keeps the fp32
+//     state rows 32s..32s+31 of the block in MFMA accumulators for the whole
+//     request; per chunk it computes the inter term of all 64 tokens
+//     restricted to its rows (no state exchange) and the update of its rows,
+//     and it sums and stores the output of the 16-token row blocks b with
+//     b % (D/32) == s;
+//   * score wave w (4 of them) computes a balanced share of the 10 causal
+//     score tiles and their P V products, and decays a quarter of the next
+//     chunk's V;
+// both roles stage chunks, in turn (see Data movement).  D = 128 runs 8 waves
+// (two per SIMD), D = 64 six.
 // The partial O^T tiles meet in LDS, where the state wave of each 16-token row
 // block adds them up.
 //
@@ -65,11 +68,26 @@
 namespace la {
 namespace {
 
-constexpr int D = kHeadDim;  // 128
-constexpr int C = 64;        // chunk length
-constexpr int VB = 32;       // state columns per workgroup
-constexpr int NVB = D / VB;  // column blocks per head
-constexpr int NT = 512;      // threads per workgroup: 4 state + 4 score waves
+constexpr int C = 64;   // chunk length
+constexpr int VB = 32;  // state columns per workgroup
+
+// Geometry for head dimension D (128 or 64).  State wave s keeps the state
+// rows 32s..32s+31 of the column block; four score waves share the score
+// tiles; state wave s also sums and stores the 16-token row blocks b with
+// b % NSW == s.
+template <int D> struct Geo {
+    static constexpr int NSW = D / 32;       // state waves
+    static constexpr int NW = NSW + 4;       // + 4 score waves
+    static constexpr int NT = 64 * NW;       // threads per workgroup
+    static constexpr int NVB = D / VB;       // column blocks per head
+    static constexpr int KS = D / 32;        // 32-wide contraction steps of a score tile
+    static constexpr int UPR = D / 8;        // 16-byte units per Q/K row
+    static constexpr int RPB = 512 / D;      // Q/K rows per 1 KB block
+    static constexpr int QBLK = C * D / 512; // 1 KB blocks per Q/K tile
+    static constexpr int OWN = 4 / NSW;      // row blocks stored per state wave
+};
+// D^-1/2
+template <int D> constexpr float kScale = D == 128 ? 0.08838834764831845f : 0.125f;
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
@@ -77,24 +95,30 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// Q and K tiles: 64 rows of 128 elements (256 B, one pass over the 64 LDS
-// banks); the 16-byte units of row r are permuted by u -> u ^ m(r), with a
-// mask per tile chosen for the reads that tile serves, each measured free of
-// bank conflicts on gfx950 (LDS conflict counters on a microbenchmark of
-// every access pattern):
+// Q and K tiles: 64 rows of D elements; the 16-byte units of row r are
+// permuted by u -> u ^ m(r), with a mask per tile chosen for the reads that
+// tile serves.  For D = 128 (a row is one 256-byte pass over the 64 LDS banks)
+// each mask was measured free of bank conflicts on gfx950 (LDS conflict
+// counters on a microbenchmark of every access pattern):
 //   Q: 16-byte score-fragment reads and 8-byte inter-term reads -> m(r) = r
 //   K: 16-byte score-fragment reads and 4x16 transposed reads
 //      -> m(r) = ((r & 7) << 1) | (r & 1)
 // (No single mask serves both tiles: the 16-byte reads want rows r and r + 8
 // to share a mask, the 8-byte reads want them apart, and the transposed reads
 // want bits 1..3 of the mask to differ within every 8 rows.)
-__device__ __forceinline__ int swz_q(int r) { return r & 15; }
-__device__ __forceinline__ int swz_k(int r) { return ((r & 7) << 1) | (r & 1); }
-__device__ __forceinline__ int q_off(int r, int col) {
-    return r * D + ((((col >> 3) ^ swz_q(r)) << 3) | (col & 7));
+// For D = 64 two rows share a pass, so a row pair p = r >> 1 plays the part
+// of a row: Q takes m(r) = p & 7, K m(r) = ((p & 3) << 1) | ((p >> 2) & 1),
+// which keeps the eight row pairs of 16 rows apart and, for the transposed
+// reads, bits 1..2 apart within every 4 pairs.
+template <int D> __device__ __forceinline__ int swz_q(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D> __device__ __forceinline__ int swz_k(int r) {
+    return D == 128 ? (((r & 7) << 1) | (r & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
 }
-__device__ __forceinline__ int k_off(int r, int col) {
-    return r * D + ((((col >> 3) ^ swz_k(r)) << 3) | (col & 7));
+template <int D> __device__ __forceinline__ int q_off(int r, int col) {
+    return r * D + ((((col >> 3) ^ swz_q<D>(r)) << 3) | (col & 7));
+}
+template <int D> __device__ __forceinline__ int k_off(int r, int col) {
+    return r * D + ((((col >> 3) ^ swz_k<D>(r)) << 3) | (col & 7));
 }
 // V tiles: 64 rows of 32 elements (64 B); units permuted by u -> u ^ swv(r),
 // which moves rows 4..7 of every 8 to the other half of the banks.
@@ -105,15 +129,24 @@ __device__ __forceinline__ int v_off(int r, int col) {
 
 constexpr int NBUF = 2;  // LDS slots: the chunk being computed and the next
 
-struct Smem {
+template <int D> struct Smem {
     uint16_t q[NBUF][C * D];  // tile ring
     uint16_t k[NBUF][C * D];
     uint16_t v[NBUF][C * VB];
     uint16_t vd_hi[C * VB];   // decayed V of the current chunk, hi/lo
     uint16_t vd_lo[C * VB];
-    f32x4 inter[4][3][2][64]; // [state wave][other row block][column tile][lane]
+    // [state wave][row block it does not store][column tile][lane]
+    f32x4 inter[Geo<D>::NSW][4 - Geo<D>::OWN][2][64];
     f32x4 intra[4][2][2][64]; // [score wave][tile group][column tile][lane]
 };
+
+// Slot of row block b among the row blocks that state wave s does not store.
+template <int D> constexpr int other_slot(int s, int b) {
+    int n = 0;
+    for (int x = 0; x < b; ++x)
+        if (x % Geo<D>::NSW != s) ++n;
+    return n;
+}
 
 __device__ __forceinline__ f32x4 mma(u16x8 a, u16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -144,8 +177,9 @@ __device__ __forceinline__ u16x4 tr_at(const uint16_t *p) {
 }
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void pin(u16x8 &x) { asm volatile("" : "+v"(x)); }
+template <int D>
 __device__ __forceinline__ u16x4 ldtr_k(const uint16_t *tile, int row0, int col0, int g, int l16) {
-    return tr_at(tile + k_off(row0 + 4 * g + (l16 >> 2), col0 + 4 * (l16 & 3)));
+    return tr_at(tile + k_off<D>(row0 + 4 * g + (l16 >> 2), col0 + 4 * (l16 & 3)));
 }
 __device__ __forceinline__ u16x4 ldtr_v(const uint16_t *tile, int row0, int col0, int g, int l16) {
     return tr_at(tile + v_off(row0 + 4 * g + (l16 >> 2), col0 + 4 * (l16 & 3)));
@@ -175,7 +209,7 @@ __device__ __forceinline__ void split4(f32x4 x, u16x4 &hi, u16x4 &lo) {
 // Workgroup id -> (pair = request*H + head, column block).  Ids are dealt to
 // XCDs round-robin (id % 8), so groups of 8 pairs are laid out with the pair
 // in the low 3 bits: the NVB blocks of one pair share id % 8.
-__device__ __forceinline__ void map_block(int id, int pairs, int &pair, int &vb) {
+template <int NVB> __device__ __forceinline__ void map_block(int id, int pairs, int &pair, int &vb) {
     const int full = (pairs / 8) * 8 * NVB;
     if (id < full) {
         const int x = id & 7, y = id >> 3;
@@ -228,7 +262,7 @@ template <> struct Tiles<3> {
 // state rows 32SW..32SW+31, part[it][nt], and the update of those rows,
 // S[k][v] = e^{-l c} S + sum_j K[j][k] Vd[j][v].  qdec[it]: weight of the inter
 // term for token i = 16 it + l16 (only without kF); dc: e^{-l c}.
-template <int SW, bool kF>
+template <int D, int SW, bool kF>
 __device__ __forceinline__ void state_chunk(const uint16_t *sq, const uint16_t *sk, const uint16_t *svh,
                                             const uint16_t *svl, const float (&qdec)[4], float dc, int g,
                                             int l16, f32x4 (&S)[2][2], f32x4 (&part)[4][2]) {
@@ -241,7 +275,7 @@ __device__ __forceinline__ void state_chunk(const uint16_t *sq, const uint16_t *
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
         const int qr = 16 * it + l16;
-        qb[it] = cat(lds4(&sq[q_off(qr, 32 * SW + 4 * g)]), lds4(&sq[q_off(qr, 32 * SW + 16 + 4 * g)]));
+        qb[it] = cat(lds4(&sq[q_off<D>(qr, 32 * SW + 4 * g)]), lds4(&sq[q_off<D>(qr, 32 * SW + 16 + 4 * g)]));
     }
     // the state as bf16 hi/lo A operand (v x k): lane (g, l16) holds rows
     // k = 32SW + 4g + r (mt 0) and 32SW + 16 + 4g + r (mt 1) of column v = l16
@@ -272,8 +306,8 @@ __device__ __forceinline__ void state_chunk(const uint16_t *sq, const uint16_t *
     for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
-            ka[s2][mt] = cat(ldtr_k(sk, 32 * s2, 32 * SW + 16 * mt, g, l16),
-                             ldtr_k(sk, 32 * s2 + 16, 32 * SW + 16 * mt, g, l16));
+            ka[s2][mt] = cat(ldtr_k<D>(sk, 32 * s2, 32 * SW + 16 * mt, g, l16),
+                             ldtr_k<D>(sk, 32 * s2 + 16, 32 * SW + 16 * mt, g, l16));
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
             vh[s2][nt] = cat(ldtr_v(svh, 32 * s2, 16 * nt, g, l16), ldtr_v(svh, 32 * s2 + 16, 16 * nt, g, l16));
@@ -309,22 +343,23 @@ __device__ __forceinline__ void state_chunk(const uint16_t *sq, const uint16_t *
 // and masked by mdec and split hi + lo, times V^T: ipart[q][nt] is the intra
 // term of i-tile Tiles<W>::git[q], column tile nt.  B operand slots 0..3 hold
 // j-tile ga's rows 4g..4g+3, slots 4..7 j-tile gb's (or zero).
-template <int W, bool kF>
+template <int D, int W, bool kF>
 __device__ __forceinline__ void score_chunk(const uint16_t *sq, const uint16_t *sk, const uint16_t *sv,
                                             const float (&mdec)[12], int g, int l16, f32x4 (&ipart)[2][2]) {
     using T = Tiles<W>;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     const u16x4 z4 = {0, 0, 0, 0};
 
-    u16x8 kf[2][4], qf[2][4];
+    constexpr int KS = Geo<D>::KS;
+    u16x8 kf[2][KS], qf[2][KS];
 #pragma unroll
     for (int a = 0; a < T::nj; ++a)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) kf[a][s] = lds8(&sk[k_off(16 * T::jl[a] + l16, 32 * s + 8 * g)]);
+        for (int s = 0; s < KS; ++s) kf[a][s] = lds8(&sk[k_off<D>(16 * T::jl[a] + l16, 32 * s + 8 * g)]);
 #pragma unroll
     for (int b = 0; b < T::ni; ++b)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) qf[b][s] = lds8(&sq[q_off(16 * T::il[b] + l16, 32 * s + 8 * g)]);
+        for (int s = 0; s < KS; ++s) qf[b][s] = lds8(&sq[q_off<D>(16 * T::il[b] + l16, 32 * s + 8 * g)]);
     u16x8 av[2][2];
 #pragma unroll
     for (int q = 0; q < T::ng; ++q) {
@@ -339,7 +374,7 @@ __device__ __forceinline__ void score_chunk(const uint16_t *sq, const uint16_t *
 #pragma unroll
     for (int t = 0; t < T::n; ++t) sc[t] = z;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
         for (int t = 0; t < T::n; ++t) sc[t] = mma(kf[T::tj[t]][s], qf[T::ti[t]][s], sc[t]);
     u16x4 p_hi[3], p_lo[3];
@@ -369,9 +404,10 @@ __device__ __forceinline__ void score_chunk(const uint16_t *sq, const uint16_t *
     }
 }
 
-// Score-wave partials of row block B, added to o.
-template <int B, int W>
-__device__ __forceinline__ void add_intra(const Smem &sm, int nt, int lane, f32x4 &o) {
+// Score-wave partials of row block B, added to o (B is a constant once the
+// caller's loops are unrolled).
+template <int W, int D>
+__device__ __forceinline__ void add_intra(const Smem<D> &sm, int B, int nt, int lane, f32x4 &o) {
     using T = Tiles<W>;
 #pragma unroll
     for (int q = 0; q < T::ng; ++q)
@@ -415,17 +451,18 @@ struct Job {
     float lam;
 };
 
-// One pass over a request for wave W of the workgroup (0..3 state waves,
-// 4..7 score waves).  Both roles meet the same barriers: two per chunk.
-template <int W, bool kF>
-__device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
-    constexpr bool kState = W < 4;
-    constexpr int R = W & 3;  // index within the role
+// One pass over a request for wave W of the workgroup (0..NSW-1 state waves,
+// NSW..NSW+3 score waves).  Both roles meet the same barriers: two per chunk.
+template <int D, int W, bool kF>
+__device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
+    using G = Geo<D>;
+    constexpr bool kState = W < G::NSW;
+    constexpr int R = kState ? W : W - G::NSW;  // index within the role
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int l16 = lane & 15, g = lane >> 4;
     const float lam = jb.lam;
-    const float scale = 0.08838834764831845f;  // 128^-1/2
+    const float scale = kScale<D>;
     const uint32_t row = static_cast<uint32_t>(jb.row);
     const int col0 = jb.col0;
 
@@ -437,10 +474,11 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
     const float vshift = kF ? 32.f : 0.f;
 
     // ---- state role: rows 32R..32R+31 of the block, tile (mt, nt) element r
-    // is S[32R + 16mt + 4g + r][col0 + 16nt + l16]
+    // is S[32R + 16mt + 4g + r][col0 + 16nt + l16]; the wave stores the row
+    // blocks R + NSW m
     f32x4 S[2][2];
     float qdec[4];
-    float fin = 0.f;
+    float fin[G::OWN];
     const float dc_full = expf(-lam * static_cast<float>(C));
     const float dc_last = expf(-lam * static_cast<float>(c_last));
     if constexpr (kState) {
@@ -454,57 +492,73 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
                         sigma * jb.state_in[(32 * R + 16 * mt + 4 * g + r) * D + col0 + 16 * nt + l16];
 #pragma unroll
         for (int it = 0; it < 4; ++it) qdec[it] = expf(-lam * static_cast<float>(16 * it + l16 + 1));
-        // output factor of row block R (token i = 16R + l16)
-        fin = kF ? scale * expf(-lam * static_cast<float>(16 * R + l16 - 31)) : scale;
+        // output factor of the stored row blocks (token i = 16B + l16)
+#pragma unroll
+        for (int m = 0; m < G::OWN; ++m) {
+            const int B = R + G::NSW * m;
+            fin[m] = kF ? scale * expf(-lam * static_cast<float>(16 * B + l16 - 31)) : scale;
+        }
     }
-    const uint32_t offo = 2u * (static_cast<uint32_t>(16 * R + l16) * row + 4 * g);
 
     // ---- score role
     float mdec[12];
     if constexpr (!kState) score_weights<R, kF>(lam, g, l16, nchunks == 1 ? c_last : C, mdec);
 
-    // Staging.  Wave R of the staging role moves Q/K rows 16R..16R+15 (4
-    // blocks of 4 rows) and V rows 16R..16R+15 (one block): lane L holds unit L
-    // of each 1 KB block, so it loads the logical unit that the swizzle places
-    // there.  Rows past the end of a short chunk repeat its last row.
-    int qk_row[4], q_unit[4], k_unit[4];
+    // Staging.  The NR waves of the staging role split each tile into 1 KB
+    // blocks (64 lanes x 16 bytes): wave R moves Q and K blocks R*QPW..+QPW-1
+    // (block b holds rows RPB b .. RPB b + RPB - 1) and V blocks R*VPW..+VPW-1
+    // (16 rows each).  Lane L holds unit L of a block, so it loads the logical
+    // unit that the swizzle places there.  Rows past the end of a short chunk
+    // repeat its last row.
+    constexpr int NR = kState ? G::NSW : 4;
+    constexpr int QPW = G::QBLK / NR;
+    constexpr int VPW = 4 / NR;
+    int qk_row[QPW], q_unit[QPW], k_unit[QPW], v_row[VPW], v_unit[VPW];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        qk_row[u] = 16 * R + 4 * u + (lane >> 4);
-        q_unit[u] = (lane & 15) ^ swz_q(qk_row[u]);
-        k_unit[u] = (lane & 15) ^ swz_k(qk_row[u]);
+    for (int u = 0; u < QPW; ++u) {
+        qk_row[u] = G::RPB * (R * QPW + u) + lane / G::UPR;
+        q_unit[u] = (lane % G::UPR) ^ swz_q<D>(qk_row[u]);
+        k_unit[u] = (lane % G::UPR) ^ swz_k<D>(qk_row[u]);
     }
-    const int v_row = 16 * R + (lane >> 2);
-    const int v_unit = (lane & 3) ^ swv(v_row);
+#pragma unroll
+    for (int u = 0; u < VPW; ++u) {
+        v_row[u] = 16 * (R * VPW + u) + (lane >> 2);
+        v_unit[u] = (lane & 3) ^ swv(v_row[u]);
+    }
     const uint32_t kvrow = static_cast<uint32_t>(jb.kvrow);
-    u16x8 rq[4], rk[4], rv;  // the chunk in flight
+    u16x8 rq[QPW], rk[QPW], rv[VPW];  // the chunk in flight
     auto load_chunk = [&](int64_t t, int c) {
         const uint16_t *qb = jb.q + t * jb.row + jb.hcol;
         const uint16_t *kb = jb.k + t * jb.kvrow + jb.kvcol;
         const uint16_t *vb = jb.v + t * jb.kvrow + jb.kvcol + col0;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < QPW; ++u) {
             const uint32_t r = static_cast<uint32_t>(qk_row[u] < c ? qk_row[u] : c - 1);
             rq[u] = *reinterpret_cast<const u16x8 *>(qb + (r * row + 8 * q_unit[u]));
             rk[u] = *reinterpret_cast<const u16x8 *>(kb + (r * kvrow + 8 * k_unit[u]));
         }
-        const uint32_t r = static_cast<uint32_t>(v_row < c ? v_row : c - 1);
-        rv = *reinterpret_cast<const u16x8 *>(vb + (r * kvrow + 8 * v_unit));
+#pragma unroll
+        for (int u = 0; u < VPW; ++u) {
+            const uint32_t r = static_cast<uint32_t>(v_row[u] < c ? v_row[u] : c - 1);
+            rv[u] = *reinterpret_cast<const u16x8 *>(vb + (r * kvrow + 8 * v_unit[u]));
+        }
     };
     auto store_chunk = [&](int buf) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the loads of the chunk landed
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int dst = (16 * R + 4 * u) * D + 8 * lane;
+        for (int u = 0; u < QPW; ++u) {
+            const int dst = 512 * (R * QPW + u) + 8 * lane;
             *reinterpret_cast<u16x8 *>(&sm.q[buf][dst]) = rq[u];
             *reinterpret_cast<u16x8 *>(&sm.k[buf][dst]) = rk[u];
         }
-        *reinterpret_cast<u16x8 *>(&sm.v[buf][16 * R * VB + 8 * lane]) = rv;
+#pragma unroll
+        for (int u = 0; u < VPW; ++u)
+            *reinterpret_cast<u16x8 *>(&sm.v[buf][512 * (R * VPW + u) + 8 * lane]) = rv[u];
     };
 
-    // Decayed V of a staged chunk: score thread u = tid - 256 converts V row
+    // Decayed V of a staged chunk: score thread u = tid - 64 NSW converts V row
     // u/4, logical unit u%4 (8 values) into hi/lo at the same (swizzled) position.
-    const int dv_row = (tid & 255) >> 2;
+    const int dv_row = ((tid - 64 * G::NSW) & 255) >> 2;
     const int dv_pos = v_off(dv_row, 8 * (tid & 3));
     // weight of that row in a full chunk and in the last one (zero past its end)
     const float vdec_full = expf(-lam * (static_cast<float>(C - 1 - dv_row) + vshift));
@@ -556,40 +610,45 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
 
         if constexpr (kState) {
             f32x4 part[4][2];
-            state_chunk<R, kF>(sm.q[buf], sm.k[buf], sm.vd_hi, sm.vd_lo, qdec, last ? dc_last : dc_full, g,
-                               l16, S, part);
+            state_chunk<D, R, kF>(sm.q[buf], sm.k[buf], sm.vd_hi, sm.vd_lo, qdec, last ? dc_last : dc_full, g,
+                                  l16, S, part);
             // hand the inter partials of the other row blocks to their state waves
 #pragma unroll
             for (int it = 0; it < 4; ++it)
-                if (it != R)
+                if (it % G::NSW != R)
 #pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) sm.inter[R][it < R ? it : it - 1][nt][lane] = part[it][nt];
+                    for (int nt = 0; nt < 2; ++nt) sm.inter[R][other_slot<D>(R, it)][nt][lane] = part[it][nt];
             lds_barrier();  // every partial of the chunk is in LDS
 
-            // row block R: sum the partials and store o.
-            // O^T tile nt, element r: value column col0 + 16nt + 4g + r, token 16R + l16
+            // the stored row blocks B: sum the partials and store o.
+            // O^T tile nt, element r: value column col0 + 16nt + 4g + r, token 16B + l16
             char *ob = reinterpret_cast<char *>(jb.out + t * jb.row + jb.hcol + col0);
-            const bool store = !last || (16 * R + l16) < c;
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                f32x4 o = part[R][nt];
+            for (int m = 0; m < G::OWN; ++m) {
+                const int B = R + G::NSW * m;
+                const bool store = !last || (16 * B + l16) < c;
+                const uint32_t offo = 2u * (static_cast<uint32_t>(16 * B + l16) * row + 4 * g);
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    if (s != R) o += sm.inter[s][R < s ? R : R - 1][nt][lane];
-                add_intra<R, 0>(sm, nt, lane, o);
-                add_intra<R, 1>(sm, nt, lane, o);
-                add_intra<R, 2>(sm, nt, lane, o);
-                add_intra<R, 3>(sm, nt, lane, o);
-                if (store) {
-                    o *= fin;
-                    const uint64_t packed = (uint64_t)cvt2(o[0], o[1]) | ((uint64_t)cvt2(o[2], o[3]) << 32);
-                    *reinterpret_cast<uint64_t *>(ob + offo + 32 * nt) = packed;
+                for (int nt = 0; nt < 2; ++nt) {
+                    f32x4 o = part[B][nt];
+#pragma unroll
+                    for (int s = 0; s < G::NSW; ++s)
+                        if (s != R) o += sm.inter[s][other_slot<D>(s, B)][nt][lane];
+                    add_intra<0>(sm, B, nt, lane, o);
+                    add_intra<1>(sm, B, nt, lane, o);
+                    add_intra<2>(sm, B, nt, lane, o);
+                    add_intra<3>(sm, B, nt, lane, o);
+                    if (store) {
+                        o *= fin[m];
+                        const uint64_t packed = (uint64_t)cvt2(o[0], o[1]) | ((uint64_t)cvt2(o[2], o[3]) << 32);
+                        *reinterpret_cast<uint64_t *>(ob + offo + 32 * nt) = packed;
+                    }
                 }
             }
         } else {
             if (last && c_last != C && nchunks > 1) score_weights<R, kF>(lam, g, l16, c_last, mdec);
             f32x4 ipart[2][2];
-            score_chunk<R, kF>(sm.q[buf], sm.k[buf], sm.v[buf], mdec, g, l16, ipart);
+            score_chunk<D, R, kF>(sm.q[buf], sm.k[buf], sm.v[buf], mdec, g, l16, ipart);
 #pragma unroll
             for (int q = 0; q < Tiles<R>::ng; ++q)
 #pragma unroll
@@ -617,28 +676,33 @@ __device__ __forceinline__ void run_wave(Smem &sm, const Job &jb) {
 
 // The passes of wave W over a request: one over [0, len), or with a snapshot
 // inside the request [0, tl) into the track slot and then [tl, len) from it.
-template <int W, bool kF>
-__device__ __forceinline__ void run_passes(Smem &sm, const Job &base, float *track, int64_t tl) {
-    if (!track) {
-        run_wave<W, kF>(sm, base);
-        return;
-    }
-    for (int i = 0; i < 2; ++i) {
-        Job jb = base;
-        jb.t0 = i == 0 ? base.t0 : base.t0 + tl;
-        jb.len = i == 0 ? tl : base.len - tl;
-        jb.state_in = i == 0 ? base.state_in : track;
-        jb.state_out = i == 0 ? track : base.state_out;
-        run_wave<W, kF>(sm, jb);
+// Wave numbers past the workgroup (D = 64 has 6 waves) do nothing.
+template <int D, int W, bool kF>
+__device__ __forceinline__ void run_passes(Smem<D> &sm, const Job &base, float *track, int64_t tl) {
+    if constexpr (W < Geo<D>::NW) {
+        if (!track) {
+            run_wave<D, W, kF>(sm, base);
+            return;
+        }
+        for (int i = 0; i < 2; ++i) {
+            Job jb = base;
+            jb.t0 = i == 0 ? base.t0 : base.t0 + tl;
+            jb.len = i == 0 ? tl : base.len - tl;
+            jb.state_in = i == 0 ? base.state_in : track;
+            jb.state_out = i == 0 ? track : base.state_out;
+            run_wave<D, W, kF>(sm, jb);
+        }
     }
 }
 
-__global__ __launch_bounds__(NT) void prefill_chunked_kernel(PrefillArgs a) {
-    __shared__ Smem sm;
+template <int D> __global__ __launch_bounds__(Geo<D>::NT) void prefill_chunked_kernel(PrefillArgs a) {
+    using G = Geo<D>;
+    constexpr int NT = G::NT;
+    __shared__ Smem<D> sm;
 
     const int H = a.num_heads;
     int pair, vb;
-    map_block(blockIdx.x, a.pairs, pair, vb);
+    map_block<G::NVB>(blockIdx.x, a.pairs, pair, vb);
     const int b = pair / H;
     const int h = pair - b * H;
     const int tid = threadIdx.x;
@@ -689,22 +753,22 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(PrefillArgs a) {
     // is below 1); anything else the explicit one
     const bool factored = base.lam >= 0.f && base.lam <= 2.f;
     switch (__builtin_amdgcn_readfirstlane(tid >> 6) + (factored ? 0 : 8)) {
-    case 0: run_passes<0, true>(sm, base, split, tl); break;
-    case 1: run_passes<1, true>(sm, base, split, tl); break;
-    case 2: run_passes<2, true>(sm, base, split, tl); break;
-    case 3: run_passes<3, true>(sm, base, split, tl); break;
-    case 4: run_passes<4, true>(sm, base, split, tl); break;
-    case 5: run_passes<5, true>(sm, base, split, tl); break;
-    case 6: run_passes<6, true>(sm, base, split, tl); break;
-    case 7: run_passes<7, true>(sm, base, split, tl); break;
-    case 8: run_passes<0, false>(sm, base, split, tl); break;
-    case 9: run_passes<1, false>(sm, base, split, tl); break;
-    case 10: run_passes<2, false>(sm, base, split, tl); break;
-    case 11: run_passes<3, false>(sm, base, split, tl); break;
-    case 12: run_passes<4, false>(sm, base, split, tl); break;
-    case 13: run_passes<5, false>(sm, base, split, tl); break;
-    case 14: run_passes<6, false>(sm, base, split, tl); break;
-    default: run_passes<7, false>(sm, base, split, tl); break;
+    case 0: run_passes<D, 0, true>(sm, base, split, tl); break;
+    case 1: run_passes<D, 1, true>(sm, base, split, tl); break;
+    case 2: run_passes<D, 2, true>(sm, base, split, tl); break;
+    case 3: run_passes<D, 3, true>(sm, base, split, tl); break;
+    case 4: run_passes<D, 4, true>(sm, base, split, tl); break;
+    case 5: run_passes<D, 5, true>(sm, base, split, tl); break;
+    case 6: run_passes<D, 6, true>(sm, base, split, tl); break;
+    case 7: run_passes<D, 7, true>(sm, base, split, tl); break;
+    case 8: run_passes<D, 0, false>(sm, base, split, tl); break;
+    case 9: run_passes<D, 1, false>(sm, base, split, tl); break;
+    case 10: run_passes<D, 2, false>(sm, base, split, tl); break;
+    case 11: run_passes<D, 3, false>(sm, base, split, tl); break;
+    case 12: run_passes<D, 4, false>(sm, base, split, tl); break;
+    case 13: run_passes<D, 5, false>(sm, base, split, tl); break;
+    case 14: run_passes<D, 6, false>(sm, base, split, tl); break;
+    default: run_passes<D, 7, false>(sm, base, split, tl); break;
     }
     if (track && tl == len) {
         // snapshot after the whole request: the final state, as stored above
@@ -716,15 +780,22 @@ __global__ __launch_bounds__(NT) void prefill_chunked_kernel(PrefillArgs a) {
     }
 }
 
-}  // namespace
-
-hipError_t launch_prefill_chunked(const PrefillArgs &a, int batch, hipStream_t stream) {
-    if (batch == 0) return hipSuccess;
+template <int D> hipError_t launch(const PrefillArgs &a, int batch, hipStream_t stream) {
     PrefillArgs copy = a;
     copy.pairs = batch * a.num_heads;
     void *args[] = {&copy};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_chunked_kernel),
-                           dim3(static_cast<unsigned>(copy.pairs) * NVB), dim3(NT), args, 0, stream);
+    return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_chunked_kernel<D>),
+                           dim3(static_cast<unsigned>(copy.pairs) * Geo<D>::NVB), dim3(Geo<D>::NT), args, 0,
+                           stream);
+}
+
+}  // namespace
+
+hipError_t launch_prefill_chunked(const PrefillArgs &a, int batch, int head_dim, hipStream_t stream) {
+    if (batch == 0) return hipSuccess;
+    if (head_dim == 128) return launch<128>(a, batch, stream);
+    if (head_dim == 64) return launch<64>(a, batch, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace la

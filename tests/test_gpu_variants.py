@@ -18,7 +18,7 @@ import oracle
 from linear_attention_amd import workloads as W
 
 from gpu_util import (TOL, assert_close, check_against_oracle, check_untouched, device_inputs,
-                      host_io, log, run_gpu)
+                      host_io, log, run_gpu, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -166,13 +166,72 @@ def test_chain_verify_grouped_heads_and_head_dim(dtype, d, HK, state_out):
 
 
 def test_head_dim_64_long_prefill_sampled_heads():
-    """A 16384-token head_dim-64 request (the token-recurrent path) on sampled heads."""
+    """A 16384-token head_dim-64 request (256 chunks of the chunked kernel) on sampled heads."""
     wl = W.make("prefill-d64-long", "prefill", "bf16", 16, [16384], 2, head_dim=64, seed=611,
                 prefix=[True], slot_idx=[1])
     log(f"case {wl.name} T={wl.total_tokens}")
     out, pool, _ = run_gpu(wl)
     check_against_oracle(wl, out, pool, heads=[0, 7, 15])
     check_untouched(wl, pool)
+
+
+# ---------------------------------------------------------------- slope regimes, invalid slots
+
+# slopes in [0, 2] take the chunked kernel's scaled-state decay, larger ones
+# its explicit per-token weights
+SLOPES = [0.0, 1e-3, 0.25, 2.0, 2.0001, 3.0, 8.0, 0.9]
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp32", 64)])
+def test_prefill_slopes_on_both_sides_of_two(dtype, d):
+    lens = [1, 64, 65, 200, 130]
+    H = len(SLOPES)
+    wl = W.make(f"slopes-{dtype}-d{d}", "prefill", dtype, H, lens, 8, head_dim=d, seed=950 + d,
+                prefix=[True, False, True, True, False])
+    log(f"case {wl.name} lens={lens} slopes={SLOPES}")
+    dv = device_inputs(wl)
+    slopes = np.array(SLOPES, dtype=np.float32)
+    out = torch.empty_like(dv["q"])
+    la.la_prefill(dv["q"], dv["k"], dv["v"], dv["cu"], dv["pool"], dv["slot"], torch.from_numpy(slopes).cuda(),
+                  out, wl.max_seqlen)
+    torch.cuda.synchronize()
+    ref_out, ref_fin = oracle.prefill(wl.q, wl.k, wl.v, wl.cu_seqlens, wl.pool, wl.slot_idx, slopes)
+    assert_close(host_io(out), ref_out, TOL[dtype], f"{wl.name} out")
+    fin = dv["pool"].index_select(0, torch.from_numpy(wl.slot_idx.astype(np.int64)).cuda()).cpu().numpy()
+    assert_close(fin, ref_fin, TOL[dtype], f"{wl.name} final state")
+    check_untouched(wl, dv["pool"])
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp32", 128)])
+def test_prefill_out_of_range_slot_gives_zero_output(dtype, d):
+    """Without the debug checks, a request whose slot index is out of range
+    gets a zero output and touches no state; the other requests are unaffected."""
+    lens = [70, 130, 5, 64]
+    wl = W.make(f"badslot-{dtype}-d{d}", "prefill", dtype, 4, lens, 6, head_dim=d, seed=960 + d,
+                prefix=[True] * 4)
+    log(f"case {wl.name} lens={lens}")
+    dv = device_inputs(wl)
+    bad = wl.slot_idx.astype(np.int32).copy()
+    bad[1], bad[3] = -1, wl.pool_slots
+    out = torch.full_like(dv["q"], 7.0)
+    la.la_prefill(dv["q"], dv["k"], dv["v"], dv["cu"], dv["pool"], i32(bad), dv["slopes"], out, wl.max_seqlen)
+    torch.cuda.synchronize()
+    cu = wl.cu_seqlens
+    got = host_io(out)
+    for b in (1, 3):
+        assert not to_f64(got[cu[b]:cu[b + 1]]).any(), f"request {b} output not zero"
+    good = [0, 2]
+    rows = np.concatenate([np.arange(cu[b], cu[b + 1]) for b in good])
+    sub_cu = np.concatenate([[0], np.cumsum([lens[b] for b in good])])
+    slopes = oracle.alibi_slopes(4, wl.layer_id, wl.num_layers)
+    ref_out, ref_fin = oracle.prefill(wl.q[rows], wl.k[rows], wl.v[rows], sub_cu, wl.pool, wl.slot_idx[good],
+                                      slopes)
+    assert_close(got[rows], ref_out, TOL[dtype], f"{wl.name} out")
+    fin = dv["pool"].index_select(0, torch.from_numpy(wl.slot_idx[good].astype(np.int64)).cuda()).cpu().numpy()
+    assert_close(fin, ref_fin, TOL[dtype], f"{wl.name} final state")
+    keep = np.setdiff1d(np.arange(wl.pool_slots), wl.slot_idx[good])
+    after = dv["pool"].index_select(0, torch.from_numpy(keep).cuda()).cpu().numpy()
+    assert np.array_equal(after.view(np.uint32), wl.pool[keep].view(np.uint32)), "untouched slot changed"
 
 
 # ---------------------------------------------------------------- tree verify
