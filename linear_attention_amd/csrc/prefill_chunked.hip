@@ -19,40 +19,42 @@
 // an exact bf16 input to ~2^-17 relative error; without it the bf16 rounding
 // of P, S_prev and Vd each add output errors of order 1e-2 on small-slope heads.
 //
-// Work split.  One workgroup per (request, head, 32-column block of S); the
-// block id is mapped so the column blocks of a head share an XCD (ids are
-// dealt to the 8 XCDs round-robin) and its L2 serves their repeated Q/K reads.
-// The waves take two roles, so that each fits in half of a SIMD's registers
-// and a SIMD can overlap one wave's MFMAs with another's vector and LDS work:
-//   * state wave s (D/32 of them: 4 for D = 128, 2 for D = 64) keeps the fp32
-//     state rows 32s..32s+31 of the block in MFMA accumulators for the whole
+// Work split.  One workgroup of 8 waves (two per SIMD) per (request, head,
+// 32-column block of S); the block id is mapped so the column blocks of a
+// head share an XCD (ids are dealt to the 8 XCDs round-robin) and its L2
+// serves their repeated Q/K reads.  The waves take two roles, so that each
+// fits in half of a SIMD's registers and a SIMD can overlap one wave's MFMAs
+// with the other's vector and LDS work:
+//   * state wave (rh, ch) keeps the fp32 state rows rh*D/2 .. rh*D/2 + D/2 - 1
+//     of column tile ch (16 columns) in MFMA accumulators for the whole
 //     request; per chunk it computes the inter term of all 64 tokens
-//     restricted to its rows (no state exchange) and the update of its rows,
-//     and it sums and stores the output of the 16-token row blocks b with
-//     b % (D/32) == s;
+//     restricted to its rows and tile (no state exchange) and the update of
+//     its rows, and it sums and stores the output of the 16-token row blocks
+//     2rh and 2rh + 1 of its tile, for which the wave with the other row half
+//     hands it the missing half of the inter term;
 //   * score wave w (4 of them) computes a balanced share of the 10 causal
 //     score tiles and their P V products, and decays a quarter of the next
 //     chunk's V;
-// both roles stage chunks, in turn (see Data movement).  D = 128 runs 8 waves
-// (two per SIMD), D = 64 six.
-// The partial O^T tiles meet in LDS, where the state wave of each 16-token row
-// block adds them up.
+// both roles stage chunks, in turn (see Data movement).
+// The partial O^T tiles meet in LDS.  Each chunk takes one barrier: the
+// partials of chunk i are summed and stored while chunk i + 1 is computed, so
+// they, the decayed V and the Q/K tiles are double-buffered by chunk parity,
+// and V, which is decayed one chunk before it is used, has a 3-slot ring.
 //
 // Data movement.  Global loads take about two microseconds under this load,
-// so the tiles of two chunks are kept in flight.  The two roles stage the
-// chunks in turn (score waves the even ones, state waves the odd ones): at
-// the start of chunk i the role that staged chunk i+1 writes it from its
-// registers to a 2-slot LDS ring, where the barrier in the middle of chunk i
-// publishes it, and then loads chunk i+3 into the same registers, two chunk
-// times before they are written.  Each wave has at most one chunk of loads in
-// flight, so vmcnt(0) before the write waits for exactly that chunk.  (Copying
-// global memory straight into LDS was slower once made safe: those copies do
-// not complete in issue order, and copies left in flight across a barrier gave
-// stale tiles under load.)
-// Operands
-// that the MFMA needs with tokens along the contraction (K^T, V^T, Vd) are
-// read from the token-major tiles with ds_read_b64_tr_b16, whose 16-lane
-// groups return the columns of a 4-row block.  Tile rows are XOR-swizzled in
+// so the tiles of two chunks are kept in flight.  The two roles stage in
+// turn: unit n (Q and K of chunk n, V of chunk n + 1) is staged by the score
+// waves when n is even, by the state waves when n is odd.  While chunk i is
+// computed, the role that holds unit i + 1 in registers writes it to LDS,
+// where the next barrier publishes it, and then loads unit i + 3 into the
+// same registers, two chunk times before they are written.  Each wave has at
+// most one unit of loads in flight, so vmcnt(0) before the write waits for
+// exactly that unit.  (Copying global memory straight into LDS was slower
+// once made safe: those copies do not complete in issue order, and copies
+// left in flight across a barrier gave stale tiles under load.)  Operands that
+// the MFMA needs with tokens along the contraction (K^T, V^T, Vd) are read
+// from the token-major tiles with ds_read_b64_tr_b16, whose 16-lane groups
+// return the columns of a 4-row block.  Tile rows are XOR-swizzled in
 // 16-byte units so that every read pattern here is free of bank conflicts.
 // Rows past the end of a short last chunk are loaded from the chunk's last
 // row (always in bounds) and given zero weight.
@@ -71,21 +73,21 @@ namespace {
 constexpr int C = 64;   // chunk length
 constexpr int VB = 32;  // state columns per workgroup
 
-// Geometry for head dimension D (128 or 64).  State wave s keeps the state
-// rows 32s..32s+31 of the column block; four score waves share the score
-// tiles; state wave s also sums and stores the 16-token row blocks b with
-// b % NSW == s.
+// Geometry for head dimension D (128 or 64).  State wave (rh, ch) keeps the
+// state rows rh*HR .. rh*HR + HR - 1 of column tile ch (16 columns) of the
+// block and stores the 16-token row blocks 2rh and 2rh + 1 of that tile; four
+// score waves share the score tiles.
 template <int D> struct Geo {
-    static constexpr int NSW = D / 32;       // state waves
-    static constexpr int NW = NSW + 4;       // + 4 score waves
-    static constexpr int NT = 64 * NW;       // threads per workgroup
     static constexpr int NVB = D / VB;       // column blocks per head
     static constexpr int KS = D / 32;        // 32-wide contraction steps of a score tile
+    static constexpr int HR = D / 2;         // state rows per state wave
+    static constexpr int HKS = HR / 32;      // 32-row contraction steps over them
+    static constexpr int HMT = HR / 16;      // 16-row tiles of them
     static constexpr int UPR = D / 8;        // 16-byte units per Q/K row
     static constexpr int RPB = 512 / D;      // Q/K rows per 1 KB block
     static constexpr int QBLK = C * D / 512; // 1 KB blocks per Q/K tile
-    static constexpr int OWN = 4 / NSW;      // row blocks stored per state wave
 };
+constexpr int NT = 512;  // threads per workgroup: 4 state + 4 score waves
 // D^-1/2
 template <int D> constexpr float kScale = D == 128 ? 0.08838834764831845f : 0.125f;
 
@@ -127,26 +129,15 @@ __device__ __forceinline__ int v_off(int r, int col) {
     return r * VB + ((((col >> 3) ^ swv(r)) << 3) | (col & 7));
 }
 
-constexpr int NBUF = 2;  // LDS slots: the chunk being computed and the next
-
 template <int D> struct Smem {
-    uint16_t q[NBUF][C * D];  // tile ring
-    uint16_t k[NBUF][C * D];
-    uint16_t v[NBUF][C * VB];
-    uint16_t vd_hi[C * VB];   // decayed V of the current chunk, hi/lo
-    uint16_t vd_lo[C * VB];
-    // [state wave][row block it does not store][column tile][lane]
-    f32x4 inter[Geo<D>::NSW][4 - Geo<D>::OWN][2][64];
-    f32x4 intra[4][2][2][64]; // [score wave][tile group][column tile][lane]
+    uint16_t q[2][C * D];        // Q/K ring: the chunk being computed and the next
+    uint16_t k[2][C * D];
+    uint16_t v[3][C * VB];       // V ring, one chunk further ahead
+    uint16_t vd_hi[2][C * VB];   // decayed V of the chunk being computed and the next
+    uint16_t vd_lo[2][C * VB];
+    f32x4 inter[2][4][2][64];    // [chunk parity][state wave][partner's row block][lane]
+    f32x4 intra[2][4][2][2][64]; // [chunk parity][score wave][tile group][column tile][lane]
 };
-
-// Slot of row block b among the row blocks that state wave s does not store.
-template <int D> constexpr int other_slot(int s, int b) {
-    int n = 0;
-    for (int x = 0; x < b; ++x)
-        if (x % Geo<D>::NSW != s) ++n;
-    return n;
-}
 
 __device__ __forceinline__ f32x4 mma(u16x8 a, u16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -258,85 +249,87 @@ template <> struct Tiles<3> {
 // and every factor stays inside the fp32/bf16 exponent range for l <= 2.
 // Without kF the weights e^{-l(i-j)} and e^{-l(i+1)} are applied directly.
 
-// One chunk for state wave SW: the inter term of all 64 tokens restricted to
-// state rows 32SW..32SW+31, part[it][nt], and the update of those rows,
-// S[k][v] = e^{-l c} S + sum_j K[j][k] Vd[j][v].  qdec[it]: weight of the inter
-// term for token i = 16 it + l16 (only without kF); dc: e^{-l c}.
-template <int D, int SW, bool kF>
+// One chunk for state wave (RH, CH): the inter term of all 64 tokens
+// restricted to its state rows R0..R0+HR-1 (R0 = RH HR) and column tile CH,
+// part[it], and the update of those rows, S[k][v] = e^{-l c} S + sum_j K[j][k]
+// Vd[j][v].  qdec[it]: weight of the inter term for token i = 16 it + l16
+// (only without kF); dc: e^{-l c}.
+template <int D, int RH, int CH, bool kF>
 __device__ __forceinline__ void state_chunk(const uint16_t *sq, const uint16_t *sk, const uint16_t *svh,
                                             const uint16_t *svl, const float (&qdec)[4], float dc, int g,
-                                            int l16, f32x4 (&S)[2][2], f32x4 (&part)[4][2]) {
+                                            int l16, f32x4 (&S)[Geo<D>::HMT], f32x4 (&part)[4]) {
+    using G = Geo<D>;
+    constexpr int R0 = RH * G::HR;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 
-    // Q^T restricted to this wave's rows (B operand: lane (g, l16) holds token
-    // 16 it + l16 and features 32SW + 4g + r, 32SW + 16 + 4g + r, the order in
-    // which the state rows sit in the A operand below)
-    u16x8 qb[4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int qr = 16 * it + l16;
-        qb[it] = cat(lds4(&sq[q_off<D>(qr, 32 * SW + 4 * g)]), lds4(&sq[q_off<D>(qr, 32 * SW + 16 + 4 * g)]));
-    }
-    // the state as bf16 hi/lo A operand (v x k): lane (g, l16) holds rows
-    // k = 32SW + 4g + r (mt 0) and 32SW + 16 + 4g + r (mt 1) of column v = l16
-    u16x8 sa_hi[2], sa_lo[2];
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-        u16x4 h0, l0, h1, l1;
-        split4(S[0][nt], h0, l0);
-        split4(S[1][nt], h1, l1);
-        sa_hi[nt] = cat(h0, h1);
-        sa_lo[nt] = cat(l0, l1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // inter term O^T[v][i] = sum_k S^T[v][k] Q^T[k][i] over this wave's rows
+    // Q^T restricted to the wave's rows (B operand of contraction step ks:
+    // lane (g, l16) holds token 16 it + l16 and features R0 + 32ks + 4g + r,
+    // R0 + 32ks + 16 + 4g + r, the order in which the state rows sit in the A
+    // operand below)
+    u16x8 qb[4][G::HKS];
 #pragma unroll
     for (int it = 0; it < 4; ++it)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            f32x4 acc = mma(sa_hi[nt], qb[it], z);
-            acc = mma(sa_lo[nt], qb[it], acc);
-            part[it][nt] = kF ? acc : acc * qdec[it];
+        for (int ks = 0; ks < G::HKS; ++ks) {
+            const int qr = 16 * it + l16;
+            qb[it][ks] = cat(lds4(&sq[q_off<D>(qr, R0 + 32 * ks + 4 * g)]),
+                             lds4(&sq[q_off<D>(qr, R0 + 32 * ks + 16 + 4 * g)]));
         }
-    // fragments of the update: K^T rows of this wave and the decayed V, with
-    // tokens along the contraction
-    u16x8 ka[2][2], vh[2][2], vl[2][2];
+    // the state as bf16 hi/lo A operand (v x k): for step ks lane (g, l16) holds
+    // rows R0 + 32ks + 4g + r (tile 2ks) and R0 + 32ks + 16 + 4g + r (tile
+    // 2ks + 1) of column v = 16 CH + l16
+    u16x8 sa_hi[G::HKS], sa_lo[G::HKS];
+#pragma unroll
+    for (int ks = 0; ks < G::HKS; ++ks) {
+        u16x4 h0, l0, h1, l1;
+        split4(S[2 * ks], h0, l0);
+        split4(S[2 * ks + 1], h1, l1);
+        sa_hi[ks] = cat(h0, h1);
+        sa_lo[ks] = cat(l0, l1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // inter term O^T[v][i] = sum_k S^T[v][k] Q^T[k][i] over the wave's rows
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        f32x4 acc = z;
+#pragma unroll
+        for (int ks = 0; ks < G::HKS; ++ks) {
+            acc = mma(sa_hi[ks], qb[it][ks], acc);
+            acc = mma(sa_lo[ks], qb[it][ks], acc);
+        }
+        part[it] = kF ? acc : acc * qdec[it];
+    }
+    // fragments of the update: K^T rows of the wave and its column tile of the
+    // decayed V, with tokens along the contraction
+    u16x8 ka[2][G::HMT], vh[2], vl[2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-            ka[s2][mt] = cat(ldtr_k<D>(sk, 32 * s2, 32 * SW + 16 * mt, g, l16),
-                             ldtr_k<D>(sk, 32 * s2 + 16, 32 * SW + 16 * mt, g, l16));
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-            vh[s2][nt] = cat(ldtr_v(svh, 32 * s2, 16 * nt, g, l16), ldtr_v(svh, 32 * s2 + 16, 16 * nt, g, l16));
-            vl[s2][nt] = cat(ldtr_v(svl, 32 * s2, 16 * nt, g, l16), ldtr_v(svl, 32 * s2 + 16, 16 * nt, g, l16));
-        }
+        for (int mt = 0; mt < G::HMT; ++mt)
+            ka[s2][mt] = cat(ldtr_k<D>(sk, 32 * s2, R0 + 16 * mt, g, l16),
+                             ldtr_k<D>(sk, 32 * s2 + 16, R0 + 16 * mt, g, l16));
+        vh[s2] = cat(ldtr_v(svh, 32 * s2, 16 * CH, g, l16), ldtr_v(svh, 32 * s2 + 16, 16 * CH, g, l16));
+        vl[s2] = cat(ldtr_v(svl, 32 * s2, 16 * CH, g, l16), ldtr_v(svl, 32 * s2 + 16, 16 * CH, g, l16));
     }
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) S[mt][nt] *= dc;
+    for (int mt = 0; mt < G::HMT; ++mt) S[mt] *= dc;
     __builtin_amdgcn_sched_barrier(0);
     lds_wait();
 #pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+        for (int mt = 0; mt < G::HMT; ++mt) pin(ka[s2][mt]);
+        pin(vh[s2]);
+        pin(vl[s2]);
+    }
+#pragma unroll
     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            pin(ka[s2][i]);
-            pin(vh[s2][i]);
-            pin(vl[s2][i]);
+        for (int mt = 0; mt < G::HMT; ++mt) {
+            S[mt] = mma(ka[s2][mt], vh[s2], S[mt]);
+            S[mt] = mma(ka[s2][mt], vl[s2], S[mt]);
         }
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                S[mt][nt] = mma(ka[s2][mt], vh[s2][nt], S[mt][nt]);
-                S[mt][nt] = mma(ka[s2][mt], vl[s2][nt], S[mt][nt]);
-            }
 }
 
 // One chunk for score wave W: its score tiles (A^T[j][i] = k_j . q_i), weighted
@@ -404,14 +397,14 @@ __device__ __forceinline__ void score_chunk(const uint16_t *sq, const uint16_t *
     }
 }
 
-// Score-wave partials of row block B, added to o (B is a constant once the
-// caller's loops are unrolled).
+// Score-wave partials of row block B and column tile nt in the partial
+// buffer par, added to o (B is a constant once the caller's loops are unrolled).
 template <int W, int D>
-__device__ __forceinline__ void add_intra(const Smem<D> &sm, int B, int nt, int lane, f32x4 &o) {
+__device__ __forceinline__ void add_intra(const Smem<D> &sm, int par, int B, int nt, int lane, f32x4 &o) {
     using T = Tiles<W>;
 #pragma unroll
     for (int q = 0; q < T::ng; ++q)
-        if (T::git[q] == B) o += sm.intra[W][q][nt][lane];
+        if (T::git[q] == B) o += sm.intra[par][W][q][nt][lane];
 }
 
 // per-lane weights of wave W's score tiles: element (t, r) is
@@ -451,13 +444,24 @@ struct Job {
     float lam;
 };
 
-// One pass over a request for wave W of the workgroup (0..NSW-1 state waves,
-// NSW..NSW+3 score waves).  Both roles meet the same barriers: two per chunk.
+// One pass over a request for wave W of the workgroup (0..3 state waves, 4..7
+// score waves).  Chunk ci is computed between barrier ci and barrier ci + 1,
+// one barrier per chunk:
+//   * state waves first finish chunk ci - 1 (sum its partials, store o), then
+//     compute chunk ci and hand the partner its inter partials;
+//   * score waves compute the intra partials of chunk ci and decay the V of
+//     chunk ci + 1;
+//   * the staging role of unit ci + 1 (Q and K of chunk ci + 1, V of chunk
+//     ci + 2) writes it to LDS and loads unit ci + 3.
+// Partials, decayed V and the Q/K tiles are double-buffered by chunk parity,
+// V is a 3-slot ring, so nothing written in one interval is read in it.
 template <int D, int W, bool kF>
 __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
     using G = Geo<D>;
-    constexpr bool kState = W < G::NSW;
-    constexpr int R = kState ? W : W - G::NSW;  // index within the role
+    constexpr bool kState = W < 4;
+    constexpr int R = W & 3;                // index within the role
+    constexpr int RH = R >> 1, CH = R & 1;  // state wave: row half, column tile
+    constexpr int PARTNER = (1 - RH) * 2 + CH;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int l16 = lane & 15, g = lane >> 4;
@@ -473,29 +477,26 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
     const float sigma = kF ? expf(-32.f * lam) : 1.f;
     const float vshift = kF ? 32.f : 0.f;
 
-    // ---- state role: rows 32R..32R+31 of the block, tile (mt, nt) element r
-    // is S[32R + 16mt + 4g + r][col0 + 16nt + l16]; the wave stores the row
-    // blocks R + NSW m
-    f32x4 S[2][2];
+    // ---- state role: tile mt element r is S[RH HR + 16mt + 4g + r][col0 + 16CH + l16];
+    // the wave stores row blocks 2RH and 2RH + 1 of column tile CH
+    f32x4 S[G::HMT];
     float qdec[4];
-    float fin[G::OWN];
+    float fin[2];
+    f32x4 keep[2];  // the wave's own inter partials of those row blocks, until stored
     const float dc_full = expf(-lam * static_cast<float>(C));
     const float dc_last = expf(-lam * static_cast<float>(c_last));
     if constexpr (kState) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < G::HMT; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    S[mt][nt][r] =
-                        sigma * jb.state_in[(32 * R + 16 * mt + 4 * g + r) * D + col0 + 16 * nt + l16];
+            for (int r = 0; r < 4; ++r)
+                S[mt][r] = sigma * jb.state_in[(RH * G::HR + 16 * mt + 4 * g + r) * D + col0 + 16 * CH + l16];
 #pragma unroll
         for (int it = 0; it < 4; ++it) qdec[it] = expf(-lam * static_cast<float>(16 * it + l16 + 1));
         // output factor of the stored row blocks (token i = 16B + l16)
 #pragma unroll
-        for (int m = 0; m < G::OWN; ++m) {
-            const int B = R + G::NSW * m;
+        for (int m = 0; m < 2; ++m) {
+            const int B = 2 * RH + m;
             fin[m] = kF ? scale * expf(-lam * static_cast<float>(16 * B + l16 - 31)) : scale;
         }
     }
@@ -504,67 +505,66 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
     float mdec[12];
     if constexpr (!kState) score_weights<R, kF>(lam, g, l16, nchunks == 1 ? c_last : C, mdec);
 
-    // Staging.  The NR waves of the staging role split each tile into 1 KB
-    // blocks (64 lanes x 16 bytes): wave R moves Q and K blocks R*QPW..+QPW-1
-    // (block b holds rows RPB b .. RPB b + RPB - 1) and V blocks R*VPW..+VPW-1
-    // (16 rows each).  Lane L holds unit L of a block, so it loads the logical
-    // unit that the swizzle places there.  Rows past the end of a short chunk
-    // repeat its last row.
-    constexpr int NR = kState ? G::NSW : 4;
-    constexpr int QPW = G::QBLK / NR;
-    constexpr int VPW = 4 / NR;
-    int qk_row[QPW], q_unit[QPW], k_unit[QPW], v_row[VPW], v_unit[VPW];
+    // Staging.  Unit n is Q and K of chunk n and V of chunk n + 1.  Wave R of
+    // the staging role moves Q/K blocks R*QPW..+QPW-1 (1 KB each: rows RPB b ..
+    // RPB b + RPB - 1) and V rows 16R..16R+15: lane L holds unit L of each 1 KB
+    // block, so it loads the logical unit that the swizzle places there.  Rows
+    // past the end of a short chunk repeat its last row.
+    constexpr int QPW = G::QBLK / 4;
+    int qk_row[QPW], q_unit[QPW], k_unit[QPW];
 #pragma unroll
     for (int u = 0; u < QPW; ++u) {
         qk_row[u] = G::RPB * (R * QPW + u) + lane / G::UPR;
         q_unit[u] = (lane % G::UPR) ^ swz_q<D>(qk_row[u]);
         k_unit[u] = (lane % G::UPR) ^ swz_k<D>(qk_row[u]);
     }
-#pragma unroll
-    for (int u = 0; u < VPW; ++u) {
-        v_row[u] = 16 * (R * VPW + u) + (lane >> 2);
-        v_unit[u] = (lane & 3) ^ swv(v_row[u]);
-    }
+    const int v_row = 16 * R + (lane >> 2);
+    const int v_unit = (lane & 3) ^ swv(v_row);
     const uint32_t kvrow = static_cast<uint32_t>(jb.kvrow);
-    u16x8 rq[QPW], rk[QPW], rv[VPW];  // the chunk in flight
-    auto load_chunk = [&](int64_t t, int c) {
-        const uint16_t *qb = jb.q + t * jb.row + jb.hcol;
-        const uint16_t *kb = jb.k + t * jb.kvrow + jb.kvcol;
-        const uint16_t *vb = jb.v + t * jb.kvrow + jb.kvcol + col0;
+    auto chunk_t = [&](int n) { return jb.t0 + static_cast<int64_t>(n) * C; };
+    auto chunk_c = [&](int n) { return n + 1 == nchunks ? c_last : C; };
+    u16x8 rq[QPW], rk[QPW], rv;  // the unit in flight
+    auto load_v = [&](int n) {
+        const int c = chunk_c(n);
+        const uint16_t *vb = jb.v + chunk_t(n) * jb.kvrow + jb.kvcol + col0;
+        const uint32_t r = static_cast<uint32_t>(v_row < c ? v_row : c - 1);
+        rv = *reinterpret_cast<const u16x8 *>(vb + (r * kvrow + 8 * v_unit));
+    };
+    auto store_v = [&](int n) { *reinterpret_cast<u16x8 *>(&sm.v[n % 3][16 * R * VB + 8 * lane]) = rv; };
+    auto load_unit = [&](int n) {
+        const int c = chunk_c(n);
+        const uint16_t *qb = jb.q + chunk_t(n) * jb.row + jb.hcol;
+        const uint16_t *kb = jb.k + chunk_t(n) * jb.kvrow + jb.kvcol;
 #pragma unroll
         for (int u = 0; u < QPW; ++u) {
             const uint32_t r = static_cast<uint32_t>(qk_row[u] < c ? qk_row[u] : c - 1);
             rq[u] = *reinterpret_cast<const u16x8 *>(qb + (r * row + 8 * q_unit[u]));
             rk[u] = *reinterpret_cast<const u16x8 *>(kb + (r * kvrow + 8 * k_unit[u]));
         }
-#pragma unroll
-        for (int u = 0; u < VPW; ++u) {
-            const uint32_t r = static_cast<uint32_t>(v_row[u] < c ? v_row[u] : c - 1);
-            rv[u] = *reinterpret_cast<const u16x8 *>(vb + (r * kvrow + 8 * v_unit[u]));
-        }
+        if (n + 1 < nchunks) load_v(n + 1);
     };
-    auto store_chunk = [&](int buf) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the loads of the chunk landed
+    auto store_unit = [&](int n) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the loads of the unit landed
+        const int buf = n & 1;
 #pragma unroll
         for (int u = 0; u < QPW; ++u) {
             const int dst = 512 * (R * QPW + u) + 8 * lane;
             *reinterpret_cast<u16x8 *>(&sm.q[buf][dst]) = rq[u];
             *reinterpret_cast<u16x8 *>(&sm.k[buf][dst]) = rk[u];
         }
-#pragma unroll
-        for (int u = 0; u < VPW; ++u)
-            *reinterpret_cast<u16x8 *>(&sm.v[buf][512 * (R * VPW + u) + 8 * lane]) = rv[u];
+        if (n + 1 < nchunks) store_v(n + 1);
     };
 
-    // Decayed V of a staged chunk: score thread u = tid - 64 NSW converts V row
-    // u/4, logical unit u%4 (8 values) into hi/lo at the same (swizzled) position.
-    const int dv_row = ((tid - 64 * G::NSW) & 255) >> 2;
+    // Decayed V: score thread u = tid - 256 converts V row u/4, logical unit u%4
+    // (8 values) into hi/lo at the same (swizzled) position.
+    const int dv_row = (tid & 255) >> 2;
     const int dv_pos = v_off(dv_row, 8 * (tid & 3));
     // weight of that row in a full chunk and in the last one (zero past its end)
     const float vdec_full = expf(-lam * (static_cast<float>(C - 1 - dv_row) + vshift));
     const float vdec_last = dv_row < c_last ? expf(-lam * (static_cast<float>(c_last - 1 - dv_row) + vshift)) : 0.f;
-    auto decay_v = [&](int buf, float vdec) {
-        const u16x8 pv = lds8(&sm.v[buf][dv_pos]);
+    auto decay_v = [&](int n) {  // V of chunk n, into slot n & 1
+        const float vdec = n + 1 == nchunks ? vdec_last : vdec_full;
+        const u16x8 pv = lds8(&sm.v[n % 3][dv_pos]);
         f32x4 x0, x1;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -574,130 +574,115 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
         u16x4 h0, l0, h1, l1;
         split4(x0, h0, l0);
         split4(x1, h1, l1);
-        *reinterpret_cast<u16x8 *>(&sm.vd_hi[dv_pos]) = cat(h0, h1);
-        *reinterpret_cast<u16x8 *>(&sm.vd_lo[dv_pos]) = cat(l0, l1);
+        *reinterpret_cast<u16x8 *>(&sm.vd_hi[n & 1][dv_pos]) = cat(h0, h1);
+        *reinterpret_cast<u16x8 *>(&sm.vd_lo[n & 1][dv_pos]) = cat(l0, l1);
     };
 
-    // chunk n is staged by the score waves when n is even, by the state waves
+    // Sum the partials of chunk p for the wave's row blocks and store o.
+    // O^T tile CH, element r: value column col0 + 16CH + 4g + r, token 16B + l16
+    auto finalize = [&](int p) {
+        const int par = p & 1;
+        const bool last = p + 1 == nchunks;
+        const int c = last ? c_last : C;
+        char *ob = reinterpret_cast<char *>(jb.out + chunk_t(p) * jb.row + jb.hcol + col0);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int B = 2 * RH + m;
+            f32x4 o = keep[m] + sm.inter[par][PARTNER][m][lane];
+            add_intra<0>(sm, par, B, CH, lane, o);
+            add_intra<1>(sm, par, B, CH, lane, o);
+            add_intra<2>(sm, par, B, CH, lane, o);
+            add_intra<3>(sm, par, B, CH, lane, o);
+            if (!last || 16 * B + l16 < c) {
+                o *= fin[m];
+                const uint32_t offo = 2u * (static_cast<uint32_t>(16 * B + l16) * row + 4 * g);
+                const uint64_t packed = (uint64_t)cvt2(o[0], o[1]) | ((uint64_t)cvt2(o[2], o[3]) << 32);
+                *reinterpret_cast<uint64_t *>(ob + offo + 32 * CH) = packed;
+            }
+        }
+    };
+
+    // unit n is staged by the score waves when n is even, by the state waves
     // when n is odd
     auto stages = [](int n) { return ((n & 1) != 0) == kState; };
-    auto chunk_t = [&](int n) { return jb.t0 + static_cast<int64_t>(n) * C; };
-    auto chunk_c = [&](int n) { return n + 1 == nchunks ? c_last : C; };
 
-    // prologue: chunk 0 in LDS, published and decayed; chunks 1 and 2 in flight
+    // prologue: V of chunk 0 and unit 0 in LDS, V of chunk 0 decayed; units 1
+    // and 2 in flight
     if (stages(0)) {
-        load_chunk(chunk_t(0), chunk_c(0));
-        store_chunk(0);
+        load_v(0);
+        store_v(0);
+        load_unit(0);
+        store_unit(0);
     }
     for (int n = 1; n <= 2; ++n)
-        if (n < nchunks && stages(n)) load_chunk(chunk_t(n), chunk_c(n));
+        if (n < nchunks && stages(n)) load_unit(n);
     __syncthreads();
-    if constexpr (!kState) decay_v(0, nchunks == 1 ? vdec_last : vdec_full);
+    if constexpr (!kState) decay_v(0);
 
-    int buf = 0;  // ring slot of chunk ci
     for (int ci = 0; ci < nchunks; ++ci) {
-        const int64_t t = jb.t0 + static_cast<int64_t>(ci) * C;
         const bool last = ci + 1 == nchunks;
-        const int c = last ? c_last : C;
-        const int nbuf = buf ^ 1;  // slot of chunk ci+1 (chunk ci-1's, read before the last barrier)
-        lds_barrier();  // chunk ci staged and decayed; previous partials consumed
-        // chunk ci+1 from registers to LDS (published at the next barrier), then
-        // chunk ci+3 from global memory to the same registers
+        lds_barrier();  // unit ci, decayed V of chunk ci and the partials of chunk ci - 1 are in LDS
+        // unit ci+1 from registers to LDS (published at the next barrier), then
+        // unit ci+3 from global memory to the same registers
         if (ci + 1 < nchunks && stages(ci + 1)) {
-            store_chunk(nbuf);
-            if (ci + 3 < nchunks) load_chunk(chunk_t(ci + 3), chunk_c(ci + 3));
+            store_unit(ci + 1);
+            if (ci + 3 < nchunks) load_unit(ci + 3);
         }
-
+        const int buf = ci & 1;
         if constexpr (kState) {
-            f32x4 part[4][2];
-            state_chunk<D, R, kF>(sm.q[buf], sm.k[buf], sm.vd_hi, sm.vd_lo, qdec, last ? dc_last : dc_full, g,
-                                  l16, S, part);
-            // hand the inter partials of the other row blocks to their state waves
+            if (ci > 0) finalize(ci - 1);
+            f32x4 part[4];
+            state_chunk<D, RH, CH, kF>(sm.q[buf], sm.k[buf], sm.vd_hi[buf], sm.vd_lo[buf], qdec,
+                                       last ? dc_last : dc_full, g, l16, S, part);
+            // row blocks of the partner to the partner, the own ones kept
 #pragma unroll
-            for (int it = 0; it < 4; ++it)
-                if (it % G::NSW != R)
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) sm.inter[R][other_slot<D>(R, it)][nt][lane] = part[it][nt];
-            lds_barrier();  // every partial of the chunk is in LDS
-
-            // the stored row blocks B: sum the partials and store o.
-            // O^T tile nt, element r: value column col0 + 16nt + 4g + r, token 16B + l16
-            char *ob = reinterpret_cast<char *>(jb.out + t * jb.row + jb.hcol + col0);
-#pragma unroll
-            for (int m = 0; m < G::OWN; ++m) {
-                const int B = R + G::NSW * m;
-                const bool store = !last || (16 * B + l16) < c;
-                const uint32_t offo = 2u * (static_cast<uint32_t>(16 * B + l16) * row + 4 * g);
-#pragma unroll
-                for (int nt = 0; nt < 2; ++nt) {
-                    f32x4 o = part[B][nt];
-#pragma unroll
-                    for (int s = 0; s < G::NSW; ++s)
-                        if (s != R) o += sm.inter[s][other_slot<D>(s, B)][nt][lane];
-                    add_intra<0>(sm, B, nt, lane, o);
-                    add_intra<1>(sm, B, nt, lane, o);
-                    add_intra<2>(sm, B, nt, lane, o);
-                    add_intra<3>(sm, B, nt, lane, o);
-                    if (store) {
-                        o *= fin[m];
-                        const uint64_t packed = (uint64_t)cvt2(o[0], o[1]) | ((uint64_t)cvt2(o[2], o[3]) << 32);
-                        *reinterpret_cast<uint64_t *>(ob + offo + 32 * nt) = packed;
-                    }
-                }
+            for (int m = 0; m < 2; ++m) {
+                sm.inter[buf][R][m][lane] = part[2 * (1 - RH) + m];
+                keep[m] = part[2 * RH + m];
             }
         } else {
             if (last && c_last != C && nchunks > 1) score_weights<R, kF>(lam, g, l16, c_last, mdec);
             f32x4 ipart[2][2];
-            score_chunk<D, R, kF>(sm.q[buf], sm.k[buf], sm.v[buf], mdec, g, l16, ipart);
+            score_chunk<D, R, kF>(sm.q[buf], sm.k[buf], sm.v[ci % 3], mdec, g, l16, ipart);
 #pragma unroll
             for (int q = 0; q < Tiles<R>::ng; ++q)
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt) sm.intra[R][q][nt][lane] = ipart[q][nt];
-            lds_barrier();  // every partial of the chunk is in LDS; chunk ci+1 staged
-            // decayed V of the next chunk (visible after the barrier above; the
-            // state waves' update of this chunk no longer reads vd)
-            if (!last) decay_v(nbuf, ci + 2 == nchunks ? vdec_last : vdec_full);
+                for (int nt = 0; nt < 2; ++nt) sm.intra[buf][R][q][nt][lane] = ipart[q][nt];
+            if (!last) decay_v(ci + 1);
         }
-        buf = nbuf;
     }
-
+    lds_barrier();  // the partials of the last chunk are in LDS
     if constexpr (kState) {
+        finalize(nchunks - 1);
         const float unscale = kF ? expf(32.f * lam) : 1.f;
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < G::HMT; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    jb.state_out[(32 * R + 16 * mt + 4 * g + r) * D + col0 + 16 * nt + l16] =
-                        S[mt][nt][r] * unscale;
+            for (int r = 0; r < 4; ++r)
+                jb.state_out[(RH * G::HR + 16 * mt + 4 * g + r) * D + col0 + 16 * CH + l16] = S[mt][r] * unscale;
     }
 }
 
 // The passes of wave W over a request: one over [0, len), or with a snapshot
 // inside the request [0, tl) into the track slot and then [tl, len) from it.
-// Wave numbers past the workgroup (D = 64 has 6 waves) do nothing.
 template <int D, int W, bool kF>
 __device__ __forceinline__ void run_passes(Smem<D> &sm, const Job &base, float *track, int64_t tl) {
-    if constexpr (W < Geo<D>::NW) {
-        if (!track) {
-            run_wave<D, W, kF>(sm, base);
-            return;
-        }
-        for (int i = 0; i < 2; ++i) {
-            Job jb = base;
-            jb.t0 = i == 0 ? base.t0 : base.t0 + tl;
-            jb.len = i == 0 ? tl : base.len - tl;
-            jb.state_in = i == 0 ? base.state_in : track;
-            jb.state_out = i == 0 ? track : base.state_out;
-            run_wave<D, W, kF>(sm, jb);
-        }
+    if (!track) {
+        run_wave<D, W, kF>(sm, base);
+        return;
+    }
+    for (int i = 0; i < 2; ++i) {
+        Job jb = base;
+        jb.t0 = i == 0 ? base.t0 : base.t0 + tl;
+        jb.len = i == 0 ? tl : base.len - tl;
+        jb.state_in = i == 0 ? base.state_in : track;
+        jb.state_out = i == 0 ? track : base.state_out;
+        run_wave<D, W, kF>(sm, jb);
     }
 }
 
-template <int D> __global__ __launch_bounds__(Geo<D>::NT) void prefill_chunked_kernel(PrefillArgs a) {
+template <int D> __global__ __launch_bounds__(NT) void prefill_chunked_kernel(PrefillArgs a) {
     using G = Geo<D>;
-    constexpr int NT = G::NT;
     __shared__ Smem<D> sm;
 
     const int H = a.num_heads;
@@ -785,8 +770,7 @@ template <int D> hipError_t launch(const PrefillArgs &a, int batch, hipStream_t 
     copy.pairs = batch * a.num_heads;
     void *args[] = {&copy};
     return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_chunked_kernel<D>),
-                           dim3(static_cast<unsigned>(copy.pairs) * Geo<D>::NVB), dim3(Geo<D>::NT), args, 0,
-                           stream);
+                           dim3(static_cast<unsigned>(copy.pairs) * Geo<D>::NVB), dim3(NT), args, 0, stream);
 }
 
 }  // namespace
