@@ -146,6 +146,15 @@ __device__ __forceinline__ f32x4 mma(u16x8 a, u16x8 b, f32x4 c) {
 
 __device__ __forceinline__ u16x8 lds8(const uint16_t *p) { return *reinterpret_cast<const u16x8 *>(p); }
 __device__ __forceinline__ u16x4 lds4(const uint16_t *p) { return *reinterpret_cast<const u16x4 *>(p); }
+// An 8-byte read that the compiler may not pair with another into a
+// ds_read2_b64: the two halves of such a pair go to the same 8-byte half of a
+// 16-byte unit in every lane, which is a 2-way bank conflict under any row
+// swizzle (measured: all of the kernel's conflict cycles came from the paired
+// Q^T reads of the inter term).
+typedef __attribute__((address_space(3))) const volatile u16x4 lds_u16x4_cv;
+__device__ __forceinline__ u16x4 lds4_single(const uint16_t *p) {
+    return *reinterpret_cast<lds_u16x4_cv *>((const lds_void *)p);
+}
 
 // Transposed 4x16 read: the 16-lane group g addresses rows row0 + 4g .. +3 and
 // columns col0 .. col0+15 (col0 a multiple of 16); lane (g, i) receives
@@ -272,8 +281,8 @@ __device__ __forceinline__ void state_chunk(const uint16_t *sq, const uint16_t *
 #pragma unroll
         for (int ks = 0; ks < G::HKS; ++ks) {
             const int qr = 16 * it + l16;
-            qb[it][ks] = cat(lds4(&sq[q_off<D>(qr, R0 + 32 * ks + 4 * g)]),
-                             lds4(&sq[q_off<D>(qr, R0 + 32 * ks + 16 + 4 * g)]));
+            qb[it][ks] = cat(lds4_single(&sq[q_off<D>(qr, R0 + 32 * ks + 4 * g)]),
+                             lds4_single(&sq[q_off<D>(qr, R0 + 32 * ks + 16 + 4 * g)]));
         }
     // the state as bf16 hi/lo A operand (v x k): for step ks lane (g, l16) holds
     // rows R0 + 32ks + 4g + r (tile 2ks) and R0 + 32ks + 16 + 4g + r (tile
