@@ -127,6 +127,27 @@ def prefill_variants(ms, ms_min, T, H):
     }
 
 
+def d2d_copy(torch, dev, nbytes=2 << 30, reps=5):
+    """A plain 2 GiB device-to-device copy (torch copy_), the achievable-bandwidth
+    reference beside the datasheet peak: GB/s of bytes read plus written."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del src, dst
+    best = min(times)
+    gbs = 2 * nbytes / (best * 1e-3) / 1e9
+    return {"bytes_copied": nbytes, "best_ms": best, "gbs": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS}
+
+
 def graph_latency(la, W, np, torch, dev, upload, warmup, reps, layers=32, batch=1):
     """Per-call time of `layers` small decode calls (one pool per call), launched
     eagerly from Python and replayed as one captured HIP graph."""
@@ -342,6 +363,7 @@ def main():
     tb = tree_bytes(wv.batch, wv.num_draft, H)
     t_gbs = tb / (ms["tree"] * 1e-3) / 1e9
     graph = graph_latency(la, W, np, torch, dev, upload, args.warmup, K)
+    copy = d2d_copy(torch, dev)
 
     result = {
         "metric": METRIC,
@@ -402,6 +424,7 @@ def main():
                          "kernel": "tree_kernel<bf16>", "algorithmic_bytes": tb},
         },
         "decode_graph": graph,
+        "d2d_copy": copy,
         "prefill_variants": prefill_variants(ms, ms_min, wp.total_tokens, H),
         "prefill_min_ms": ms_min["prefill"],
         "cpu_baseline": None,
