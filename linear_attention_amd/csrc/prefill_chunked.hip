@@ -19,12 +19,12 @@
 // an exact bf16 input to ~2^-17 relative error; without it the bf16 rounding
 // of P, S_prev and Vd each add output errors of order 1e-2 on small-slope heads.
 //
-// Work split.  One workgroup of 8 waves (two per SIMD) per (request, head,
+// Work split.  One workgroup of 12 waves (three per SIMD) per (request, head,
 // 32-column block of S); the block id is mapped so the column blocks of a
 // head share an XCD (ids are dealt to the 8 XCDs round-robin) and its L2
-// serves their repeated Q/K reads.  The waves take two roles, so that each
-// fits in half of a SIMD's registers and a SIMD can overlap one wave's MFMAs
-// with the other's vector and LDS work:
+// serves their repeated Q/K reads.  The waves take three roles, so that each
+// fits in a third of a SIMD's registers and a SIMD can overlap one wave's
+// MFMAs with the others' vector, LDS and memory work:
 //   * state wave (rh, ch) keeps the fp32 state rows rh*D/2 .. rh*D/2 + D/2 - 1
 //     of column tile ch (16 columns) in MFMA accumulators for the whole
 //     request; per chunk it computes the inter term of all 64 tokens
@@ -33,23 +33,22 @@
 //     2rh and 2rh + 1 of its tile, for which the wave with the other row half
 //     hands it the missing half of the inter term;
 //   * score wave w (4 of them) computes a balanced share of the 10 causal
-//     score tiles and their P V products, and decays a quarter of the next
-//     chunk's V;
-// both roles stage chunks, in turn (see Data movement).
+//     score tiles and their P V products;
+//   * staging waves (4 of them) move the tiles from global memory to LDS and
+//     decay the next chunk's V, so that neither compute role waits on a load.
 // The partial O^T tiles meet in LDS.  Each chunk takes one barrier: the
 // partials of chunk i are summed and stored while chunk i + 1 is computed, so
 // they, the decayed V and the Q/K tiles are double-buffered by chunk parity,
 // and V, which is decayed one chunk before it is used, has a 3-slot ring.
 //
 // Data movement.  Global loads take about two microseconds under this load,
-// so the tiles of two chunks are kept in flight.  The two roles stage in
-// turn: unit n (Q and K of chunk n, V of chunk n + 1) is staged by the score
-// waves when n is even, by the state waves when n is odd.  While chunk i is
-// computed, the role that holds unit i + 1 in registers writes it to LDS,
-// where the next barrier publishes it, and then loads unit i + 3 into the
-// same registers, two chunk times before they are written.  Each wave has at
-// most one unit of loads in flight, so vmcnt(0) before the write waits for
-// exactly that unit.  (Copying global memory straight into LDS was slower
+// so the tiles of two chunks are kept in flight.  The staging waves work in
+// two groups of two: unit n (Q and K of chunk n, V of chunk n + 1) is staged
+// by group n % 2.  While chunk i is computed, the group that holds unit i + 1
+// in registers writes it to LDS, where the next barrier publishes it, and then
+// loads unit i + 3 into the same registers, two chunk times before they are
+// written.  Each wave has at most one unit of loads in flight, so vmcnt(0)
+// before the write waits for exactly that unit.  (Copying global memory straight into LDS was slower
 // once made safe: those copies do not complete in issue order, and copies
 // left in flight across a barrier gave stale tiles under load.)  Operands that
 // the MFMA needs with tokens along the contraction (K^T, V^T, Vd) are read
@@ -87,7 +86,7 @@ template <int D> struct Geo {
     static constexpr int RPB = 512 / D;      // Q/K rows per 1 KB block
     static constexpr int QBLK = C * D / 512; // 1 KB blocks per Q/K tile
 };
-constexpr int NT = 512;  // threads per workgroup: 4 state + 4 score waves
+constexpr int NT = 768;  // threads per workgroup: 4 state, 4 score and 4 staging waves
 // D^-1/2
 template <int D> constexpr float kScale = D == 128 ? 0.08838834764831845f : 0.125f;
 
@@ -434,7 +433,7 @@ __device__ __forceinline__ void score_weights(float lam, int g, int l16, int c, 
 
 // Workgroup barrier for LDS data only.  __syncthreads() would also make every
 // wave wait for its outstanding global loads (it is a release fence), which
-// would drain the score waves' loads of the chunk after next.
+// would drain the staging waves' loads of the chunk after next.
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -454,21 +453,24 @@ struct Job {
 };
 
 // One pass over a request for wave W of the workgroup (0..3 state waves, 4..7
-// score waves).  Chunk ci is computed between barrier ci and barrier ci + 1,
-// one barrier per chunk:
+// score waves, 8..11 staging waves).  Chunk ci is computed between barrier ci
+// and barrier ci + 1, one barrier per chunk:
 //   * state waves first finish chunk ci - 1 (sum its partials, store o), then
 //     compute chunk ci and hand the partner its inter partials;
-//   * score waves compute the intra partials of chunk ci and decay the V of
-//     chunk ci + 1;
-//   * the staging role of unit ci + 1 (Q and K of chunk ci + 1, V of chunk
-//     ci + 2) writes it to LDS and loads unit ci + 3.
+//   * score waves compute the intra partials of chunk ci;
+//   * the staging group of unit ci + 1 (Q and K of chunk ci + 1, V of chunk
+//     ci + 2) writes it to LDS and loads unit ci + 3, and all staging waves
+//     decay the V of chunk ci + 1.
 // Partials, decayed V and the Q/K tiles are double-buffered by chunk parity,
 // V is a 3-slot ring, so nothing written in one interval is read in it.
 template <int D, int W, bool kF>
 __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
     using G = Geo<D>;
     constexpr bool kState = W < 4;
+    constexpr bool kScore = W >= 4 && W < 8;
+    constexpr bool kHelper = W >= 8;        // staging and V decay
     constexpr int R = W & 3;                // index within the role
+    constexpr int HG = R >> 1, HI = R & 1;  // staging wave: group (unit parity), index in the group
     constexpr int RH = R >> 1, CH = R & 1;  // state wave: row half, column tile
     constexpr int PARTNER = (1 - RH) * 2 + CH;
     const int tid = threadIdx.x;
@@ -512,34 +514,45 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
 
     // ---- score role
     float mdec[12];
-    if constexpr (!kState) score_weights<R, kF>(lam, g, l16, nchunks == 1 ? c_last : C, mdec);
+    if constexpr (kScore) score_weights<R, kF>(lam, g, l16, nchunks == 1 ? c_last : C, mdec);
 
-    // Staging.  Unit n is Q and K of chunk n and V of chunk n + 1.  Wave R of
-    // the staging role moves Q/K blocks R*QPW..+QPW-1 (1 KB each: rows RPB b ..
-    // RPB b + RPB - 1) and V rows 16R..16R+15: lane L holds unit L of each 1 KB
-    // block, so it loads the logical unit that the swizzle places there.  Rows
-    // past the end of a short chunk repeat its last row.
-    constexpr int QPW = G::QBLK / 4;
+    // Staging.  Unit n is Q and K of chunk n and V of chunk n + 1.  Wave HI of
+    // a staging group moves Q/K blocks HI*QPW..+QPW-1 (1 KB each: rows RPB b ..
+    // RPB b + RPB - 1) and V rows 32HI..32HI+31: lane L holds unit L of each 1
+    // KB block, so it loads the logical unit that the swizzle places there.
+    // Rows past the end of a short chunk repeat its last row.
+    constexpr int QPW = G::QBLK / 2;
     int qk_row[QPW], q_unit[QPW], k_unit[QPW];
 #pragma unroll
     for (int u = 0; u < QPW; ++u) {
-        qk_row[u] = G::RPB * (R * QPW + u) + lane / G::UPR;
+        qk_row[u] = G::RPB * (HI * QPW + u) + lane / G::UPR;
         q_unit[u] = (lane % G::UPR) ^ swz_q<D>(qk_row[u]);
         k_unit[u] = (lane % G::UPR) ^ swz_k<D>(qk_row[u]);
     }
-    const int v_row = 16 * R + (lane >> 2);
-    const int v_unit = (lane & 3) ^ swv(v_row);
+    int v_row[2], v_unit[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        v_row[u] = 16 * (2 * HI + u) + (lane >> 2);
+        v_unit[u] = (lane & 3) ^ swv(v_row[u]);
+    }
     const uint32_t kvrow = static_cast<uint32_t>(jb.kvrow);
     auto chunk_t = [&](int n) { return jb.t0 + static_cast<int64_t>(n) * C; };
     auto chunk_c = [&](int n) { return n + 1 == nchunks ? c_last : C; };
-    u16x8 rq[QPW], rk[QPW], rv;  // the unit in flight
+    u16x8 rq[QPW], rk[QPW], rv[2];  // the unit in flight
     auto load_v = [&](int n) {
         const int c = chunk_c(n);
         const uint16_t *vb = jb.v + chunk_t(n) * jb.kvrow + jb.kvcol + col0;
-        const uint32_t r = static_cast<uint32_t>(v_row < c ? v_row : c - 1);
-        rv = *reinterpret_cast<const u16x8 *>(vb + (r * kvrow + 8 * v_unit));
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const uint32_t r = static_cast<uint32_t>(v_row[u] < c ? v_row[u] : c - 1);
+            rv[u] = *reinterpret_cast<const u16x8 *>(vb + (r * kvrow + 8 * v_unit[u]));
+        }
     };
-    auto store_v = [&](int n) { *reinterpret_cast<u16x8 *>(&sm.v[n % 3][16 * R * VB + 8 * lane]) = rv; };
+    auto store_v = [&](int n) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+            *reinterpret_cast<u16x8 *>(&sm.v[n % 3][512 * (2 * HI + u) + 8 * lane]) = rv[u];
+    };
     auto load_unit = [&](int n) {
         const int c = chunk_c(n);
         const uint16_t *qb = jb.q + chunk_t(n) * jb.row + jb.hcol;
@@ -557,15 +570,15 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
         const int buf = n & 1;
 #pragma unroll
         for (int u = 0; u < QPW; ++u) {
-            const int dst = 512 * (R * QPW + u) + 8 * lane;
+            const int dst = 512 * (HI * QPW + u) + 8 * lane;
             *reinterpret_cast<u16x8 *>(&sm.q[buf][dst]) = rq[u];
             *reinterpret_cast<u16x8 *>(&sm.k[buf][dst]) = rk[u];
         }
         if (n + 1 < nchunks) store_v(n + 1);
     };
 
-    // Decayed V: score thread u = tid - 256 converts V row u/4, logical unit u%4
-    // (8 values) into hi/lo at the same (swizzled) position.
+    // Decayed V: staging thread u = tid - 512 converts V row u/4, logical unit
+    // u%4 (8 values) into hi/lo at the same (swizzled) position.
     const int dv_row = (tid & 255) >> 2;
     const int dv_pos = v_off(dv_row, 8 * (tid & 3));
     // weight of that row in a full chunk and in the last one (zero past its end)
@@ -611,9 +624,8 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
         }
     };
 
-    // unit n is staged by the score waves when n is even, by the state waves
-    // when n is odd
-    auto stages = [](int n) { return ((n & 1) != 0) == kState; };
+    // unit n is staged by staging group n % 2
+    auto stages = [](int n) { return kHelper && (n & 1) == HG; };
 
     // prologue: V of chunk 0 and unit 0 in LDS, V of chunk 0 decayed; units 1
     // and 2 in flight
@@ -626,16 +638,19 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
     for (int n = 1; n <= 2; ++n)
         if (n < nchunks && stages(n)) load_unit(n);
     __syncthreads();
-    if constexpr (!kState) decay_v(0);
+    if constexpr (kHelper) decay_v(0);
 
     for (int ci = 0; ci < nchunks; ++ci) {
         const bool last = ci + 1 == nchunks;
         lds_barrier();  // unit ci, decayed V of chunk ci and the partials of chunk ci - 1 are in LDS
         // unit ci+1 from registers to LDS (published at the next barrier), then
         // unit ci+3 from global memory to the same registers
-        if (ci + 1 < nchunks && stages(ci + 1)) {
-            store_unit(ci + 1);
-            if (ci + 3 < nchunks) load_unit(ci + 3);
+        if constexpr (kHelper) {
+            if (ci + 1 < nchunks && stages(ci + 1)) {
+                store_unit(ci + 1);
+                if (ci + 3 < nchunks) load_unit(ci + 3);
+            }
+            if (!last) decay_v(ci + 1);
         }
         const int buf = ci & 1;
         if constexpr (kState) {
@@ -649,7 +664,8 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
                 sm.inter[buf][R][m][lane] = part[2 * (1 - RH) + m];
                 keep[m] = part[2 * RH + m];
             }
-        } else {
+        }
+        if constexpr (kScore) {
             if (last && c_last != C && nchunks > 1) score_weights<R, kF>(lam, g, l16, c_last, mdec);
             f32x4 ipart[2][2];
             score_chunk<D, R, kF>(sm.q[buf], sm.k[buf], sm.v[ci % 3], mdec, g, l16, ipart);
@@ -657,7 +673,6 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
             for (int q = 0; q < Tiles<R>::ng; ++q)
 #pragma unroll
                 for (int nt = 0; nt < 2; ++nt) sm.intra[buf][R][q][nt][lane] = ipart[q][nt];
-            if (!last) decay_v(ci + 1);
         }
     }
     lds_barrier();  // the partials of the last chunk are in LDS
@@ -746,7 +761,7 @@ template <int D> __global__ __launch_bounds__(NT) void prefill_chunked_kernel(Pr
     // slopes in [0, 2] take the factored decay path (the largest ALiBi slope
     // is below 1); anything else the explicit one
     const bool factored = base.lam >= 0.f && base.lam <= 2.f;
-    switch (__builtin_amdgcn_readfirstlane(tid >> 6) + (factored ? 0 : 8)) {
+    switch (__builtin_amdgcn_readfirstlane(tid >> 6) + (factored ? 0 : 12)) {
     case 0: run_passes<D, 0, true>(sm, base, split, tl); break;
     case 1: run_passes<D, 1, true>(sm, base, split, tl); break;
     case 2: run_passes<D, 2, true>(sm, base, split, tl); break;
@@ -755,14 +770,22 @@ template <int D> __global__ __launch_bounds__(NT) void prefill_chunked_kernel(Pr
     case 5: run_passes<D, 5, true>(sm, base, split, tl); break;
     case 6: run_passes<D, 6, true>(sm, base, split, tl); break;
     case 7: run_passes<D, 7, true>(sm, base, split, tl); break;
-    case 8: run_passes<D, 0, false>(sm, base, split, tl); break;
-    case 9: run_passes<D, 1, false>(sm, base, split, tl); break;
-    case 10: run_passes<D, 2, false>(sm, base, split, tl); break;
-    case 11: run_passes<D, 3, false>(sm, base, split, tl); break;
-    case 12: run_passes<D, 4, false>(sm, base, split, tl); break;
-    case 13: run_passes<D, 5, false>(sm, base, split, tl); break;
-    case 14: run_passes<D, 6, false>(sm, base, split, tl); break;
-    default: run_passes<D, 7, false>(sm, base, split, tl); break;
+    case 8: run_passes<D, 8, true>(sm, base, split, tl); break;
+    case 9: run_passes<D, 9, true>(sm, base, split, tl); break;
+    case 10: run_passes<D, 10, true>(sm, base, split, tl); break;
+    case 11: run_passes<D, 11, true>(sm, base, split, tl); break;
+    case 12: run_passes<D, 0, false>(sm, base, split, tl); break;
+    case 13: run_passes<D, 1, false>(sm, base, split, tl); break;
+    case 14: run_passes<D, 2, false>(sm, base, split, tl); break;
+    case 15: run_passes<D, 3, false>(sm, base, split, tl); break;
+    case 16: run_passes<D, 4, false>(sm, base, split, tl); break;
+    case 17: run_passes<D, 5, false>(sm, base, split, tl); break;
+    case 18: run_passes<D, 6, false>(sm, base, split, tl); break;
+    case 19: run_passes<D, 7, false>(sm, base, split, tl); break;
+    case 20: run_passes<D, 8, false>(sm, base, split, tl); break;
+    case 21: run_passes<D, 9, false>(sm, base, split, tl); break;
+    case 22: run_passes<D, 10, false>(sm, base, split, tl); break;
+    default: run_passes<D, 11, false>(sm, base, split, tl); break;
     }
     if (track && tl == len) {
         // snapshot after the whole request: the final state, as stored above
