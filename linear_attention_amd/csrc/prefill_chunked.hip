@@ -34,8 +34,9 @@
 //     hands it the missing half of the inter term;
 //   * score wave w (4 of them) computes a balanced share of the 10 causal
 //     score tiles and their P V products;
-//   * staging waves (4 of them) move the tiles from global memory to LDS and
-//     decay the next chunk's V, so that neither compute role waits on a load.
+//   * staging waves (4 of them, two groups of two) move the tiles from global
+//     memory to LDS and decay the next chunk's V, so that neither compute role
+//     waits on a load: in each chunk one group stages and the other decays.
 // The partial O^T tiles meet in LDS.  Each chunk takes one barrier: the
 // partials of chunk i are summed and stored while chunk i + 1 is computed, so
 // they, the decayed V and the Q/K tiles are double-buffered by chunk parity,
@@ -459,8 +460,8 @@ struct Job {
 //     compute chunk ci and hand the partner its inter partials;
 //   * score waves compute the intra partials of chunk ci;
 //   * the staging group of unit ci + 1 (Q and K of chunk ci + 1, V of chunk
-//     ci + 2) writes it to LDS and loads unit ci + 3, and all staging waves
-//     decay the V of chunk ci + 1.
+//     ci + 2) writes it to LDS and loads unit ci + 3, and the other group
+//     decays the V of chunk ci + 1.
 // Partials, decayed V and the Q/K tiles are double-buffered by chunk parity,
 // V is a 3-slot ring, so nothing written in one interval is read in it.
 template <int D, int W, bool kF>
@@ -577,27 +578,36 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
         if (n + 1 < nchunks) store_v(n + 1);
     };
 
-    // Decayed V: staging thread u = tid - 512 converts V row u/4, logical unit
-    // u%4 (8 values) into hi/lo at the same (swizzled) position.
-    const int dv_row = (tid & 255) >> 2;
-    const int dv_pos = v_off(dv_row, 8 * (tid & 3));
-    // weight of that row in a full chunk and in the last one (zero past its end)
-    const float vdec_full = expf(-lam * (static_cast<float>(C - 1 - dv_row) + vshift));
-    const float vdec_last = dv_row < c_last ? expf(-lam * (static_cast<float>(c_last - 1 - dv_row) + vshift)) : 0.f;
-    auto decay_v = [&](int n) {  // V of chunk n, into slot n & 1
-        const float vdec = n + 1 == nchunks ? vdec_last : vdec_full;
-        const u16x8 pv = lds8(&sm.v[n % 3][dv_pos]);
-        f32x4 x0, x1;
+    // Decayed V: thread u (0..127) of the decaying staging group converts V
+    // rows u/4 and u/4 + 32, logical unit u%4 (8 values each), into hi/lo at
+    // the same (swizzled) position.
+    const int du = ((W - 8) & 1) * 64 + lane;
+    float vdec_full[2], vdec_last[2];
+    int dv_pos[2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            x0[e] = bf16_to_f32(pv[e]) * vdec;
-            x1[e] = bf16_to_f32(pv[4 + e]) * vdec;
+    for (int e = 0; e < 2; ++e) {
+        const int dv_row = (du >> 2) + 32 * e;
+        dv_pos[e] = v_off(dv_row, 8 * (du & 3));
+        vdec_full[e] = expf(-lam * (static_cast<float>(C - 1 - dv_row) + vshift));
+        vdec_last[e] = dv_row < c_last ? expf(-lam * (static_cast<float>(c_last - 1 - dv_row) + vshift)) : 0.f;
+    }
+    auto decay_v = [&](int n) {  // V of chunk n, into slot n & 1
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float vdec = n + 1 == nchunks ? vdec_last[e] : vdec_full[e];
+            const u16x8 pv = lds8(&sm.v[n % 3][dv_pos[e]]);
+            f32x4 x0, x1;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                x0[k] = bf16_to_f32(pv[k]) * vdec;
+                x1[k] = bf16_to_f32(pv[4 + k]) * vdec;
+            }
+            u16x4 h0, l0, h1, l1;
+            split4(x0, h0, l0);
+            split4(x1, h1, l1);
+            *reinterpret_cast<u16x8 *>(&sm.vd_hi[n & 1][dv_pos[e]]) = cat(h0, h1);
+            *reinterpret_cast<u16x8 *>(&sm.vd_lo[n & 1][dv_pos[e]]) = cat(l0, l1);
         }
-        u16x4 h0, l0, h1, l1;
-        split4(x0, h0, l0);
-        split4(x1, h1, l1);
-        *reinterpret_cast<u16x8 *>(&sm.vd_hi[n & 1][dv_pos]) = cat(h0, h1);
-        *reinterpret_cast<u16x8 *>(&sm.vd_lo[n & 1][dv_pos]) = cat(l0, l1);
     };
 
     // Sum the partials of chunk p for the wave's row blocks and store o.
@@ -638,7 +648,8 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
     for (int n = 1; n <= 2; ++n)
         if (n < nchunks && stages(n)) load_unit(n);
     __syncthreads();
-    if constexpr (kHelper) decay_v(0);
+    if constexpr (kHelper)
+        if (HG == 1) decay_v(0);
 
     for (int ci = 0; ci < nchunks; ++ci) {
         const bool last = ci + 1 == nchunks;
@@ -650,7 +661,8 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
                 store_unit(ci + 1);
                 if (ci + 3 < nchunks) load_unit(ci + 3);
             }
-            if (!last) decay_v(ci + 1);
+            // the group that does not stage this chunk decays the next V
+            if (!last && HG == (ci & 1)) decay_v(ci + 1);
         }
         const int buf = ci & 1;
         if constexpr (kState) {
