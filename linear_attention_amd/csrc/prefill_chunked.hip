@@ -222,12 +222,15 @@ template <int NVB> __device__ __forceinline__ void map_block(int id, int pairs, 
     }
 }
 
-// Score tiles (j-tile, i-tile), j <= i, dealt to the waves 3/3/2/2.  Each
-// wave loads the K fragments of its distinct j-tiles (jl) and the Q fragments
-// of its distinct i-tiles (il) once; tile t uses jl[tj[t]] and il[ti[t]].  The
-// P V products group a wave's tiles by i-tile (at most two j-tiles, which
-// together fill one 32-token contraction): group q covers i-tile git[q] with
-// tiles ga[q] and gb[q] (-1: none).
+// Score tiles (j-tile, i-tile), j <= i, dealt to the waves 3/3/2/2: wave 0
+// takes the causal block of i-tiles 0-1, wave 1 that of i-tiles 2-3, and
+// waves 2 and 3 the full rows j-tiles 0-1 of i-tiles 2 and 3.  Each wave loads
+// the K fragments of its distinct j-tiles (jl) and the Q fragments of its
+// distinct i-tiles (il) once; tile t uses jl[tj[t]] and il[ti[t]].  The P V
+// products group a wave's tiles by i-tile (at most two j-tiles, which together
+// fill one 32-token contraction): group q covers i-tile git[q] with tiles
+// ga[q] and gb[q] (-1: none).  So an output row block gets at most two intra
+// partials (row blocks 2 and 3: one from wave 1, one from wave 2 or 3).
 template <int W> struct Tiles;
 template <> struct Tiles<0> {
     static constexpr int n = 3, tj[3] = {0, 0, 1}, ti[3] = {0, 1, 1};
@@ -240,14 +243,14 @@ template <> struct Tiles<1> {
     static constexpr int ng = 2, git[2] = {2, 3}, ga[2] = {0, 1}, gb[2] = {-1, 2};
 };
 template <> struct Tiles<2> {
-    static constexpr int n = 2, tj[3] = {0, 0, 0}, ti[3] = {0, 1, 0};
-    static constexpr int nj = 1, jl[2] = {0, 0}, ni = 2, il[2] = {2, 3};
-    static constexpr int ng = 2, git[2] = {2, 3}, ga[2] = {0, 1}, gb[2] = {-1, -1};
+    static constexpr int n = 2, tj[3] = {0, 1, 0}, ti[3] = {0, 0, 0};
+    static constexpr int nj = 2, jl[2] = {0, 1}, ni = 1, il[2] = {2, 2};
+    static constexpr int ng = 1, git[2] = {2, -1}, ga[2] = {0, -1}, gb[2] = {1, -1};
 };
 template <> struct Tiles<3> {
-    static constexpr int n = 2, tj[3] = {0, 0, 0}, ti[3] = {0, 1, 0};
-    static constexpr int nj = 1, jl[2] = {1, 1}, ni = 2, il[2] = {2, 3};
-    static constexpr int ng = 2, git[2] = {2, 3}, ga[2] = {0, 1}, gb[2] = {-1, -1};
+    static constexpr int n = 2, tj[3] = {0, 1, 0}, ti[3] = {0, 0, 0};
+    static constexpr int nj = 2, jl[2] = {0, 1}, ni = 1, il[2] = {3, 3};
+    static constexpr int ng = 1, git[2] = {3, -1}, ga[2] = {0, -1}, gb[2] = {1, -1};
 };
 
 // Decay handling.  With kF ("factored", used for 0 <= l <= 2) the state is
