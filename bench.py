@@ -127,6 +127,20 @@ def prefill_variants(ms, ms_min, T, H):
     }
 
 
+def varlen_prefill(ms, ms_min, wl):
+    """Rate of the packed varlen prefill (8 requests of U[1, 4096] tokens, H=16)."""
+    T, H, B = wl.total_tokens, wl.num_heads, wl.batch
+    nbytes = prefill_bytes(T, H, B)
+    gbs = nbytes / (ms["prefill_varlen"] * 1e-3) / 1e9
+    return {"workload": f"varlen prefill H={H} d={D} bf16, {B} requests, lengths "
+                        f"{[int(wl.cu_seqlens[i + 1] - wl.cu_seqlens[i]) for i in range(B)]}, T={T}",
+            "avg_ms": ms["prefill_varlen"], "min_ms": ms_min["prefill_varlen"],
+            "tokens_per_s": T / (ms["prefill_varlen"] * 1e-3),
+            "algorithmic_bytes": nbytes, "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "mfma_useful_frac": prefill_useful_flops(T, H) / (ms["prefill_varlen"] * 1e-3) / 1e12
+                                / BF16_PEAK_TFLOPS}
+
+
 def d2d_copy(torch, dev, nbytes=2 << 30, reps=5):
     """A plain 2 GiB device-to-device copy (torch copy_), the achievable-bandwidth
     reference beside the datasheet peak: GB/s of bytes read plus written."""
@@ -312,7 +326,18 @@ def main():
             la.la_prefill(V4["q64"], V4["k64"], V4["v64"], V4["cu64"], V4["pool64"], P["slot"], P["slopes"],
                           V4["out64"], T64, stream=stream)
 
-        extra += [("prefill_track", run_track), ("prefill_gqa", run_gqa), ("prefill_d64", run_d64)]
+        # the packed varlen workload: H=16, 8 requests of U[1, 4096] tokens, half with prefix states
+        w2 = W.config(2)
+        P2 = upload(w2)
+        P2["out"] = torch.empty_like(P2["q"])
+
+        def run_varlen():
+            la.la_prefill(P2["q"], P2["k"], P2["v"], P2["cu"], P2["pool"], P2["slot"], P2["slopes"],
+                          P2["out"], w2.max_seqlen, stream=stream)
+
+        extra += [("prefill_track", run_track), ("prefill_gqa", run_gqa), ("prefill_d64", run_d64),
+                  ("prefill_varlen", run_varlen)]
+        V4["varlen"] = w2
     for _ in range(args.warmup):
         for _, fn in calls + extra:
             fn()
@@ -426,6 +451,7 @@ def main():
         "decode_graph": graph,
         "d2d_copy": copy,
         "prefill_variants": prefill_variants(ms, ms_min, wp.total_tokens, H),
+        "varlen_prefill": varlen_prefill(ms, ms_min, V4["varlen"]) if "prefill_varlen" in ms else None,
         "prefill_min_ms": ms_min["prefill"],
         "cpu_baseline": None,
     }

@@ -206,9 +206,11 @@ __device__ __forceinline__ void split4(f32x4 x, u16x4 &hi, u16x4 &lo) {
     lo = __builtin_bit_cast(u16x4, (uint64_t)l01 | ((uint64_t)l23 << 32));
 }
 
-// Workgroup id -> (pair = request*H + head, column block).  Ids are dealt to
-// XCDs round-robin (id % 8), so groups of 8 pairs are laid out with the pair
-// in the low 3 bits: the NVB blocks of one pair share id % 8.
+// Workgroup id -> (pair = request*H + head, column block; "request" is the
+// request's rank in length order for batches that are sorted, see
+// request_of_rank).  Ids are dealt to XCDs round-robin (id % 8), so groups of
+// 8 pairs are laid out with the pair in the low 3 bits: the NVB blocks of one
+// pair share id % 8.
 template <int NVB> __device__ __forceinline__ void map_block(int id, int pairs, int &pair, int &vb) {
     const int full = (pairs / 8) * 8 * NVB;
     if (id < full) {
@@ -720,20 +722,62 @@ __device__ __forceinline__ void run_passes(Smem<D> &sm, const Job &base, float *
     }
 }
 
+// Request b's token range [t0, t1): cu_seqlens clamped to [0, total_tokens]
+// and made non-decreasing, so that a malformed entry gives an empty request.
+__device__ __forceinline__ void request_range(const PrefillArgs &a, int b, int64_t &t0, int64_t &t1) {
+    t0 = a.cu_seqlens[b];
+    t1 = a.cu_seqlens[b + 1];
+    t0 = t0 < 0 ? 0 : (t0 > a.total_tokens ? a.total_tokens : t0);
+    t1 = t1 < t0 ? t0 : (t1 > a.total_tokens ? a.total_tokens : t1);
+}
+
+// Longest request first.  A batch of up to kSortMax requests is taken in
+// order of decreasing length (ties by index): rank r of that order is the
+// request that workgroups with pair index r*H .. r*H + H - 1 serve.  When the
+// grid is larger than the GPU holds at once, the long requests then start in
+// the first round of workgroups and the short ones fill in behind them, so
+// the launch ends with the longest request instead of a long request that
+// was dispatched late.  Every workgroup ranks the (at most kSortMax) lengths
+// itself; the results do not depend on the order.
+constexpr int kSortMax = 256;
+__device__ __forceinline__ int request_of_rank(const PrefillArgs &a, int batch, int r, int *lens, int *pick) {
+    const int tid = threadIdx.x;
+    for (int i = tid; i < batch; i += NT) {
+        int64_t t0, t1;
+        request_range(a, i, t0, t1);
+        lens[i] = static_cast<int>(t1 - t0);
+    }
+    __syncthreads();
+    if (tid < batch) {
+        const int li = lens[tid];
+        int rank = 0;
+        for (int j = 0; j < batch; ++j) {
+            const int lj = lens[j];
+            rank += (lj > li || (lj == li && j < tid)) ? 1 : 0;
+        }
+        if (rank == r) *pick = tid;
+    }
+    __syncthreads();
+    return *pick;
+}
+
 template <int D> __global__ __launch_bounds__(NT) void prefill_chunked_kernel(PrefillArgs a) {
     using G = Geo<D>;
     __shared__ Smem<D> sm;
+    __shared__ int sort_lens[kSortMax];
+    __shared__ int sort_pick;
 
     const int H = a.num_heads;
     int pair, vb;
     map_block<G::NVB>(blockIdx.x, a.pairs, pair, vb);
-    const int b = pair / H;
+    const int batch = a.pairs / H;
+    int b = pair / H;
     const int h = pair - b * H;
     const int tid = threadIdx.x;
+    if (batch > 1 && batch <= kSortMax) b = request_of_rank(a, batch, b, sort_lens, &sort_pick);
 
-    int64_t t0 = a.cu_seqlens[b], t1 = a.cu_seqlens[b + 1];
-    t0 = t0 < 0 ? 0 : (t0 > a.total_tokens ? a.total_tokens : t0);
-    t1 = t1 < t0 ? t0 : (t1 > a.total_tokens ? a.total_tokens : t1);
+    int64_t t0, t1;
+    request_range(a, b, t0, t1);
     const int64_t len = t1 - t0;
 
     const size_t row = static_cast<size_t>(H) * D;

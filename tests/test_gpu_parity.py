@@ -156,6 +156,20 @@ def test_request_order_invariance():
     np.testing.assert_array_equal(pool2.cpu().numpy(), pool.cpu().numpy())
 
 
+@pytest.mark.parametrize("B,H,head_dim", [(200, 8, 128), (257, 2, 128), (48, 4, 64)])
+def test_many_requests_with_tied_lengths(B, H, head_dim):
+    """Batches that the prefill dispatches longest request first (B <= 256)
+    and one just past that limit, in natural order.  The lengths repeat a few
+    values, so most requests tie, and include empty requests; the grids are
+    several times what the GPU holds at once."""
+    rng = np.random.default_rng(1000 + B)
+    lens = rng.choice([0, 1, 63, 64, 65, 130, 200], size=B)
+    prefix = [b % 3 == 0 for b in range(B)]
+    wl = W.make(f"ties-{B}-{H}-{head_dim}", "prefill", "bf16", H, lens, B + 5, head_dim=head_dim,
+                seed=1100 + B, prefix=prefix)
+    _full_check(wl)
+
+
 def test_debug_mode_rejects_bad_metadata():
     wl = W.make("debug", "prefill", "bf16", 2, [3, 4], 4, seed=95)
     d = device_inputs(wl)
