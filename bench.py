@@ -111,6 +111,7 @@ def prefill_variants(ms, ms_min, T, H):
     T64 = 16384
     gqa_bytes = T * H * (2 * D * 2) + T * 8 * (2 * D * 2) + H * 2 * STATE_BYTES
     d64_bytes = T64 * H * 4 * 64 * 2 + H * 2 * 64 * 64 * 4
+    tp8_bytes = prefill_bytes(T, 8, 1)
     return {
         "track_snapshot": {"workload": f"long prefill T={T} H={H} d={D}, snapshot after {T // 2} tokens",
                            "avg_ms": ms["prefill_track"], "min_ms": ms_min["prefill_track"],
@@ -119,11 +120,22 @@ def prefill_variants(ms, ms_min, T, H):
         "grouped_heads": {"workload": f"prefill T={T} H={H} Hkv=8 d={D}", "avg_ms": ms["prefill_gqa"],
                           "min_ms": ms_min["prefill_gqa"], "tokens_per_s": T / (ms["prefill_gqa"] * 1e-3),
                           "hbm_gbs": gqa_bytes / (ms["prefill_gqa"] * 1e-3) / 1e9},
-        "head_dim_64": {"workload": f"prefill T={T64} H={H} d=64 (chunked kernel, 2 column blocks per head)",
+        "head_dim_64": {"workload": f"prefill T={T64} H={H} d=64 (chunked kernel, 2 column blocks per head, "
+                                    "2 sequence segments)",
                         "avg_ms": ms["prefill_d64"], "min_ms": ms_min["prefill_d64"],
                         "tokens_per_s": T64 / (ms["prefill_d64"] * 1e-3),
                         "hbm_gbs": d64_bytes / (ms["prefill_d64"] * 1e-3) / 1e9,
-                        "hbm_frac": d64_bytes / (ms["prefill_d64"] * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                        "hbm_frac": d64_bytes / (ms["prefill_d64"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "unsegmented_avg_ms": ms["prefill_d64_unseg"],
+                        "segment_speedup": ms["prefill_d64_unseg"] / ms["prefill_d64"]},
+        "tp8_share": {"workload": f"prefill T={T} H=8 d={D}: heads 0..7 of the long request, one GPU's "
+                                  "share at 8-way head parallelism (8 sequence segments)",
+                      "avg_ms": ms["prefill_tp8"], "min_ms": ms_min["prefill_tp8"],
+                      "tokens_per_s": T / (ms["prefill_tp8"] * 1e-3),
+                      "hbm_gbs": tp8_bytes / (ms["prefill_tp8"] * 1e-3) / 1e9,
+                      "hbm_frac": tp8_bytes / (ms["prefill_tp8"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                      "unsegmented_avg_ms": ms["prefill_tp8_unseg"],
+                      "segment_speedup": ms["prefill_tp8_unseg"] / ms["prefill_tp8"]},
     }
 
 
@@ -335,8 +347,29 @@ def main():
             la.la_prefill(P2["q"], P2["k"], P2["v"], P2["cu"], P2["pool"], P2["slot"], P2["slopes"],
                           P2["out"], w2.max_seqlen, stream=stream)
 
+        # the tensor-parallel share of the long request: heads 0..7 (8 of 64), which
+        # fills 32 CUs unless the request is split into sequence segments
+        V4.update({"q8h": P["q"][:, :8].contiguous(), "k8h": P["k"][:, :8].contiguous(),
+                   "v8h": P["v"][:, :8].contiguous(), "pool8h": torch.zeros((2, 8, D, D), device=dev),
+                   "slopes8h": P["slopes"][:8].contiguous()})
+        V4["out8h"] = torch.empty_like(V4["q8h"])
+
+        def run_tp8():
+            la.la_prefill(V4["q8h"], V4["k8h"], V4["v8h"], P["cu"], V4["pool8h"], P["slot"], V4["slopes8h"],
+                          V4["out8h"], wp.max_seqlen, stream=stream)
+
+        def unsegmented(fn):
+            def run():
+                os.environ["LA_PREFILL_MAX_SEGMENTS"] = "1"
+                try:
+                    fn()
+                finally:
+                    del os.environ["LA_PREFILL_MAX_SEGMENTS"]
+            return run
+
         extra += [("prefill_track", run_track), ("prefill_gqa", run_gqa), ("prefill_d64", run_d64),
-                  ("prefill_varlen", run_varlen)]
+                  ("prefill_varlen", run_varlen), ("prefill_tp8", run_tp8),
+                  ("prefill_tp8_unseg", unsegmented(run_tp8)), ("prefill_d64_unseg", unsegmented(run_d64))]
         V4["varlen"] = w2
     for _ in range(args.warmup):
         for _, fn in calls + extra:

@@ -161,7 +161,7 @@ la_status la_prefill(const void *q, const void *k, const void *v, la_dtype dtype
         a.track_slot_idx = track_slot_idx;
         a.slopes = slopes;
         a.out = static_cast<uint16_t *>(out);
-        return from_hip(la::launch_prefill_chunked(a, batch, head_dim, stream));
+        return from_hip(la::launch_prefill_chunked(a, batch, head_dim, max_seqlen, stream));
     }
     la::RecurrentArgs a{};
     a.q = q;

@@ -57,7 +57,12 @@ struct PrefillArgs {
     const int32_t *track_lens, *track_slot_idx;
     const float *slopes;
     uint16_t *out;
+    int segments;   // sequence segments per request (set by the launcher)
+    float *seg_ws;  // their workspace, [batch*H][segments][D][D] fp32
 };
-hipError_t launch_prefill_chunked(const PrefillArgs &a, int batch, int head_dim, hipStream_t stream);
+// max_seqlen: the longest request (decides how many segments a launch that
+// underfills the GPU splits requests into; any value gives the same results)
+hipError_t launch_prefill_chunked(const PrefillArgs &a, int batch, int head_dim, int max_seqlen,
+                                  hipStream_t stream);
 
 }  // namespace la

@@ -64,6 +64,8 @@
 // the first pass stores its final state to the track slot and the second
 // starts from it.  Grouped heads read k and v at the query head's group
 // (head h / (H / Hkv)) with their own token stride.
+#include <cstdlib>
+
 #include "common.h"
 #include "launch.h"
 
@@ -265,10 +267,10 @@ template <> struct Tiles<3> {
 
 // One chunk for state wave (RH, CH): the inter term of all 64 tokens
 // restricted to its state rows R0..R0+HR-1 (R0 = RH HR) and column tile CH,
-// part[it], and the update of those rows, S[k][v] = e^{-l c} S + sum_j K[j][k]
-// Vd[j][v].  qdec[it]: weight of the inter term for token i = 16 it + l16
-// (only without kF); dc: e^{-l c}.
-template <int D, int RH, int CH, bool kF>
+// part[it] (only with kInter), and the update of those rows, S[k][v] = e^{-l c}
+// S + sum_j K[j][k] Vd[j][v].  qdec[it]: weight of the inter term for token
+// i = 16 it + l16 (only without kF); dc: e^{-l c}.
+template <int D, int RH, int CH, bool kF, bool kInter>
 __device__ __forceinline__ void state_chunk(const uint16_t *sq, const uint16_t *sk, const uint16_t *svh,
                                             const uint16_t *svl, const float (&qdec)[4], float dc, int g,
                                             int l16, f32x4 (&S)[Geo<D>::HMT], f32x4 (&part)[4]) {
@@ -276,43 +278,45 @@ __device__ __forceinline__ void state_chunk(const uint16_t *sq, const uint16_t *
     constexpr int R0 = RH * G::HR;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 
-    // Q^T restricted to the wave's rows (B operand of contraction step ks:
-    // lane (g, l16) holds token 16 it + l16 and features R0 + 32ks + 4g + r,
-    // R0 + 32ks + 16 + 4g + r, the order in which the state rows sit in the A
-    // operand below)
-    u16x8 qb[4][G::HKS];
+    if constexpr (kInter) {
+        // Q^T restricted to the wave's rows (B operand of contraction step ks:
+        // lane (g, l16) holds token 16 it + l16 and features R0 + 32ks + 4g + r,
+        // R0 + 32ks + 16 + 4g + r, the order in which the state rows sit in the A
+        // operand below)
+        u16x8 qb[4][G::HKS];
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
+        for (int it = 0; it < 4; ++it)
+#pragma unroll
+            for (int ks = 0; ks < G::HKS; ++ks) {
+                const int qr = 16 * it + l16;
+                qb[it][ks] = cat(lds4_single(&sq[q_off<D>(qr, R0 + 32 * ks + 4 * g)]),
+                                 lds4_single(&sq[q_off<D>(qr, R0 + 32 * ks + 16 + 4 * g)]));
+            }
+        // the state as bf16 hi/lo A operand (v x k): for step ks lane (g, l16) holds
+        // rows R0 + 32ks + 4g + r (tile 2ks) and R0 + 32ks + 16 + 4g + r (tile
+        // 2ks + 1) of column v = 16 CH + l16
+        u16x8 sa_hi[G::HKS], sa_lo[G::HKS];
 #pragma unroll
         for (int ks = 0; ks < G::HKS; ++ks) {
-            const int qr = 16 * it + l16;
-            qb[it][ks] = cat(lds4_single(&sq[q_off<D>(qr, R0 + 32 * ks + 4 * g)]),
-                             lds4_single(&sq[q_off<D>(qr, R0 + 32 * ks + 16 + 4 * g)]));
+            u16x4 h0, l0, h1, l1;
+            split4(S[2 * ks], h0, l0);
+            split4(S[2 * ks + 1], h1, l1);
+            sa_hi[ks] = cat(h0, h1);
+            sa_lo[ks] = cat(l0, l1);
         }
-    // the state as bf16 hi/lo A operand (v x k): for step ks lane (g, l16) holds
-    // rows R0 + 32ks + 4g + r (tile 2ks) and R0 + 32ks + 16 + 4g + r (tile
-    // 2ks + 1) of column v = 16 CH + l16
-    u16x8 sa_hi[G::HKS], sa_lo[G::HKS];
-#pragma unroll
-    for (int ks = 0; ks < G::HKS; ++ks) {
-        u16x4 h0, l0, h1, l1;
-        split4(S[2 * ks], h0, l0);
-        split4(S[2 * ks + 1], h1, l1);
-        sa_hi[ks] = cat(h0, h1);
-        sa_lo[ks] = cat(l0, l1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_sched_barrier(0);
 
-    // inter term O^T[v][i] = sum_k S^T[v][k] Q^T[k][i] over the wave's rows
+        // inter term O^T[v][i] = sum_k S^T[v][k] Q^T[k][i] over the wave's rows
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        f32x4 acc = z;
+        for (int it = 0; it < 4; ++it) {
+            f32x4 acc = z;
 #pragma unroll
-        for (int ks = 0; ks < G::HKS; ++ks) {
-            acc = mma(sa_hi[ks], qb[it][ks], acc);
-            acc = mma(sa_lo[ks], qb[it][ks], acc);
+            for (int ks = 0; ks < G::HKS; ++ks) {
+                acc = mma(sa_hi[ks], qb[it][ks], acc);
+                acc = mma(sa_lo[ks], qb[it][ks], acc);
+            }
+            part[it] = kF ? acc : acc * qdec[it];
         }
-        part[it] = kF ? acc : acc * qdec[it];
     }
     // fragments of the update: K^T rows of the wave and its column tile of the
     // decayed V, with tokens along the contraction
@@ -449,7 +453,7 @@ __device__ __forceinline__ void lds_barrier() {
 struct Job {
     const uint16_t *q, *k, *v;
     uint16_t *out;
-    const float *state_in;  // state before the pass
+    const float *state_in;  // state before the pass (not read by a state-only pass: zero)
     float *state_out;       // state after the pass
     int64_t t0, len;        // tokens [t0, t0 + len), len >= 1
     size_t row, hcol;       // q/out token stride and head column
@@ -469,7 +473,9 @@ struct Job {
 //     decays the V of chunk ci + 1.
 // Partials, decayed V and the Q/K tiles are double-buffered by chunk parity,
 // V is a 3-slot ring, so nothing written in one interval is read in it.
-template <int D, int W, bool kF>
+// With kDelta the pass computes the state only: no Q tiles, no scores, no
+// inter term and no output, with the same chunk loop and barriers.
+template <int D, int W, bool kF, bool kDelta>
 __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
     using G = Geo<D>;
     constexpr bool kState = W < 4;
@@ -507,7 +513,8 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
         for (int mt = 0; mt < G::HMT; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                S[mt][r] = sigma * jb.state_in[(RH * G::HR + 16 * mt + 4 * g + r) * D + col0 + 16 * CH + l16];
+                S[mt][r] = kDelta ? 0.f
+                                  : sigma * jb.state_in[(RH * G::HR + 16 * mt + 4 * g + r) * D + col0 + 16 * CH + l16];
 #pragma unroll
         for (int it = 0; it < 4; ++it) qdec[it] = expf(-lam * static_cast<float>(16 * it + l16 + 1));
         // output factor of the stored row blocks (token i = 16B + l16)
@@ -566,7 +573,7 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
 #pragma unroll
         for (int u = 0; u < QPW; ++u) {
             const uint32_t r = static_cast<uint32_t>(qk_row[u] < c ? qk_row[u] : c - 1);
-            rq[u] = *reinterpret_cast<const u16x8 *>(qb + (r * row + 8 * q_unit[u]));
+            if constexpr (!kDelta) rq[u] = *reinterpret_cast<const u16x8 *>(qb + (r * row + 8 * q_unit[u]));
             rk[u] = *reinterpret_cast<const u16x8 *>(kb + (r * kvrow + 8 * k_unit[u]));
         }
         if (n + 1 < nchunks) load_v(n + 1);
@@ -577,7 +584,7 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
 #pragma unroll
         for (int u = 0; u < QPW; ++u) {
             const int dst = 512 * (HI * QPW + u) + 8 * lane;
-            *reinterpret_cast<u16x8 *>(&sm.q[buf][dst]) = rq[u];
+            if constexpr (!kDelta) *reinterpret_cast<u16x8 *>(&sm.q[buf][dst]) = rq[u];
             *reinterpret_cast<u16x8 *>(&sm.k[buf][dst]) = rk[u];
         }
         if (n + 1 < nchunks) store_v(n + 1);
@@ -671,18 +678,20 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
         }
         const int buf = ci & 1;
         if constexpr (kState) {
-            if (ci > 0) finalize(ci - 1);
+            if (!kDelta && ci > 0) finalize(ci - 1);
             f32x4 part[4];
-            state_chunk<D, RH, CH, kF>(sm.q[buf], sm.k[buf], sm.vd_hi[buf], sm.vd_lo[buf], qdec,
-                                       last ? dc_last : dc_full, g, l16, S, part);
+            state_chunk<D, RH, CH, kF, !kDelta>(sm.q[buf], sm.k[buf], sm.vd_hi[buf], sm.vd_lo[buf], qdec,
+                                                last ? dc_last : dc_full, g, l16, S, part);
             // row blocks of the partner to the partner, the own ones kept
+            if constexpr (!kDelta) {
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                sm.inter[buf][R][m][lane] = part[2 * (1 - RH) + m];
-                keep[m] = part[2 * RH + m];
+                for (int m = 0; m < 2; ++m) {
+                    sm.inter[buf][R][m][lane] = part[2 * (1 - RH) + m];
+                    keep[m] = part[2 * RH + m];
+                }
             }
         }
-        if constexpr (kScore) {
+        if constexpr (kScore && !kDelta) {
             if (last && c_last != C && nchunks > 1) score_weights<R, kF>(lam, g, l16, c_last, mdec);
             f32x4 ipart[2][2];
             score_chunk<D, R, kF>(sm.q[buf], sm.k[buf], sm.v[ci % 3], mdec, g, l16, ipart);
@@ -694,7 +703,7 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
     }
     lds_barrier();  // the partials of the last chunk are in LDS
     if constexpr (kState) {
-        finalize(nchunks - 1);
+        if constexpr (!kDelta) finalize(nchunks - 1);
         const float unscale = kF ? expf(32.f * lam) : 1.f;
 #pragma unroll
         for (int mt = 0; mt < G::HMT; ++mt)
@@ -706,10 +715,10 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
 
 // The passes of wave W over a request: one over [0, len), or with a snapshot
 // inside the request [0, tl) into the track slot and then [tl, len) from it.
-template <int D, int W, bool kF>
+template <int D, int W, bool kF, bool kDelta>
 __device__ __forceinline__ void run_passes(Smem<D> &sm, const Job &base, float *track, int64_t tl) {
     if (!track) {
-        run_wave<D, W, kF>(sm, base);
+        run_wave<D, W, kF, kDelta>(sm, base);
         return;
     }
     for (int i = 0; i < 2; ++i) {
@@ -718,7 +727,41 @@ __device__ __forceinline__ void run_passes(Smem<D> &sm, const Job &base, float *
         jb.len = i == 0 ? tl : base.len - tl;
         jb.state_in = i == 0 ? base.state_in : track;
         jb.state_out = i == 0 ? track : base.state_out;
-        run_wave<D, W, kF>(sm, jb);
+        run_wave<D, W, kF, kDelta>(sm, jb);
+    }
+}
+
+// The wave's role and decay path for one pass: wave index and, for slopes
+// outside [0, 2], the explicit (not factored) decay.  Slopes in [0, 2] take
+// the factored path (the largest ALiBi slope is below 1).
+template <int D, bool kDelta>
+__device__ __forceinline__ void dispatch(Smem<D> &sm, const Job &base, float *split, int64_t tl) {
+    const bool factored = base.lam >= 0.f && base.lam <= 2.f;
+    switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) + (factored ? 0 : 12)) {
+    case 0: run_passes<D, 0, true, kDelta>(sm, base, split, tl); break;
+    case 1: run_passes<D, 1, true, kDelta>(sm, base, split, tl); break;
+    case 2: run_passes<D, 2, true, kDelta>(sm, base, split, tl); break;
+    case 3: run_passes<D, 3, true, kDelta>(sm, base, split, tl); break;
+    case 4: run_passes<D, 4, true, kDelta>(sm, base, split, tl); break;
+    case 5: run_passes<D, 5, true, kDelta>(sm, base, split, tl); break;
+    case 6: run_passes<D, 6, true, kDelta>(sm, base, split, tl); break;
+    case 7: run_passes<D, 7, true, kDelta>(sm, base, split, tl); break;
+    case 8: run_passes<D, 8, true, kDelta>(sm, base, split, tl); break;
+    case 9: run_passes<D, 9, true, kDelta>(sm, base, split, tl); break;
+    case 10: run_passes<D, 10, true, kDelta>(sm, base, split, tl); break;
+    case 11: run_passes<D, 11, true, kDelta>(sm, base, split, tl); break;
+    case 12: run_passes<D, 0, false, kDelta>(sm, base, split, tl); break;
+    case 13: run_passes<D, 1, false, kDelta>(sm, base, split, tl); break;
+    case 14: run_passes<D, 2, false, kDelta>(sm, base, split, tl); break;
+    case 15: run_passes<D, 3, false, kDelta>(sm, base, split, tl); break;
+    case 16: run_passes<D, 4, false, kDelta>(sm, base, split, tl); break;
+    case 17: run_passes<D, 5, false, kDelta>(sm, base, split, tl); break;
+    case 18: run_passes<D, 6, false, kDelta>(sm, base, split, tl); break;
+    case 19: run_passes<D, 7, false, kDelta>(sm, base, split, tl); break;
+    case 20: run_passes<D, 8, false, kDelta>(sm, base, split, tl); break;
+    case 21: run_passes<D, 9, false, kDelta>(sm, base, split, tl); break;
+    case 22: run_passes<D, 10, false, kDelta>(sm, base, split, tl); break;
+    default: run_passes<D, 11, false, kDelta>(sm, base, split, tl); break;
     }
 }
 
@@ -761,6 +804,36 @@ __device__ __forceinline__ int request_of_rank(const PrefillArgs &a, int batch, 
     return *pick;
 }
 
+// Sequence segments.  A launch whose (request, head, column block) units
+// fill only part of the GPU splits every request into up to a.segments
+// segments of whole chunks, cps chunks each, and runs them side by side:
+//   1. prefill_delta_kernel: the state contribution of every segment but the
+//      last, dS_s = sum over its tokens t of e^{-l(end_s - 1 - t)} k_t v_t^T
+//      (the recurrence from a zero state, no outputs);
+//   2. prefill_combine_kernel: the state before each segment, by the same
+//      recurrence at segment granularity: S_0 is the pool state and
+//      S_{s+1} = e^{-l cps C} S_s + dS_s;
+//   3. prefill_chunked_kernel: every segment from its own initial state, as a
+//      request of its own; the last segment stores the final state.
+// All three read and write the workspace a.seg_ws, [pair][segment][D][D]
+// fp32, in stream order; the pool slot is read by step 2 only and written by
+// step 3 only.
+struct SegGeom {
+    int nchunks;  // chunks of the request
+    int cps;      // chunks per segment
+    int ne;       // non-empty segments
+};
+__device__ __forceinline__ SegGeom seg_geom(int64_t len, int segments) {
+    SegGeom g;
+    g.nchunks = static_cast<int>((len + C - 1) / C);
+    g.cps = (g.nchunks + segments - 1) / segments;
+    g.ne = g.cps > 0 ? (g.nchunks + g.cps - 1) / g.cps : 0;
+    return g;
+}
+template <int D> __device__ __forceinline__ float *seg_slice(const PrefillArgs &a, int pair, int s) {
+    return a.seg_ws + (static_cast<size_t>(pair) * a.segments + s) * (D * D);
+}
+
 template <int D> __global__ __launch_bounds__(NT) void prefill_chunked_kernel(PrefillArgs a) {
     using G = Geo<D>;
     __shared__ Smem<D> sm;
@@ -768,8 +841,10 @@ template <int D> __global__ __launch_bounds__(NT) void prefill_chunked_kernel(Pr
     __shared__ int sort_pick;
 
     const int H = a.num_heads;
+    const int units = a.pairs * G::NVB;
+    const int seg = static_cast<int>(blockIdx.x) / units;  // 0 without segments
     int pair, vb;
-    map_block<G::NVB>(blockIdx.x, a.pairs, pair, vb);
+    map_block<G::NVB>(static_cast<int>(blockIdx.x) - seg * units, a.pairs, pair, vb);
     const int batch = a.pairs / H;
     int b = pair / H;
     const int h = pair - b * H;
@@ -778,7 +853,17 @@ template <int D> __global__ __launch_bounds__(NT) void prefill_chunked_kernel(Pr
 
     int64_t t0, t1;
     request_range(a, b, t0, t1);
-    const int64_t len = t1 - t0;
+    int64_t len = t1 - t0;
+    const bool segmented = a.segments > 1;
+    int nseg = 1;
+    if (segmented) {
+        const SegGeom sg = seg_geom(len, a.segments);
+        if (seg >= sg.ne) return;  // past the end of the request (or an empty one)
+        const int64_t s0 = static_cast<int64_t>(seg) * sg.cps * C;
+        t0 += s0;
+        len = len - s0 < static_cast<int64_t>(sg.cps) * C ? len - s0 : static_cast<int64_t>(sg.cps) * C;
+        nseg = sg.ne;
+    }
 
     const size_t row = static_cast<size_t>(H) * D;
     const size_t hcol = static_cast<size_t>(h) * D;
@@ -796,7 +881,7 @@ template <int D> __global__ __launch_bounds__(NT) void prefill_chunked_kernel(Pr
     float *state = a.pool + (static_cast<size_t>(slot) * H + h) * (D * D);
     float *track = nullptr;
     int64_t tl = len;
-    if (a.track_lens) {
+    if (a.track_lens) {  // (never with segments)
         const int ts = a.track_slot_idx[b];
         const int64_t n = a.track_lens[b];
         if (ts >= 0 && ts < a.pool_slots && n >= 0 && n <= len) {
@@ -813,39 +898,16 @@ template <int D> __global__ __launch_bounds__(NT) void prefill_chunked_kernel(Pr
     }
     if (len <= 0) return;  // empty request: no-op
     const int hk = h / (H / a.num_kv_heads);
-    const Job base{a.q, a.k, a.v, a.out, state, state, t0, len, row, hcol,
+    // with segments: initial state from the workspace; only the last segment
+    // stores the final state in the pool, the others over their own (already
+    // read) initial state
+    float *s_in = segmented ? seg_slice<D>(a, b * H + h, seg) : state;
+    float *s_out = !segmented || seg == nseg - 1 ? state : s_in;
+    const Job base{a.q, a.k, a.v, a.out, s_in, s_out, t0, len, row, hcol,
                    static_cast<size_t>(a.num_kv_heads) * D, static_cast<size_t>(hk) * D, col0, a.slopes[h]};
     // a snapshot strictly inside the request splits it into two passes
     float *split = track && tl > 0 && tl < len ? track : nullptr;
-    // slopes in [0, 2] take the factored decay path (the largest ALiBi slope
-    // is below 1); anything else the explicit one
-    const bool factored = base.lam >= 0.f && base.lam <= 2.f;
-    switch (__builtin_amdgcn_readfirstlane(tid >> 6) + (factored ? 0 : 12)) {
-    case 0: run_passes<D, 0, true>(sm, base, split, tl); break;
-    case 1: run_passes<D, 1, true>(sm, base, split, tl); break;
-    case 2: run_passes<D, 2, true>(sm, base, split, tl); break;
-    case 3: run_passes<D, 3, true>(sm, base, split, tl); break;
-    case 4: run_passes<D, 4, true>(sm, base, split, tl); break;
-    case 5: run_passes<D, 5, true>(sm, base, split, tl); break;
-    case 6: run_passes<D, 6, true>(sm, base, split, tl); break;
-    case 7: run_passes<D, 7, true>(sm, base, split, tl); break;
-    case 8: run_passes<D, 8, true>(sm, base, split, tl); break;
-    case 9: run_passes<D, 9, true>(sm, base, split, tl); break;
-    case 10: run_passes<D, 10, true>(sm, base, split, tl); break;
-    case 11: run_passes<D, 11, true>(sm, base, split, tl); break;
-    case 12: run_passes<D, 0, false>(sm, base, split, tl); break;
-    case 13: run_passes<D, 1, false>(sm, base, split, tl); break;
-    case 14: run_passes<D, 2, false>(sm, base, split, tl); break;
-    case 15: run_passes<D, 3, false>(sm, base, split, tl); break;
-    case 16: run_passes<D, 4, false>(sm, base, split, tl); break;
-    case 17: run_passes<D, 5, false>(sm, base, split, tl); break;
-    case 18: run_passes<D, 6, false>(sm, base, split, tl); break;
-    case 19: run_passes<D, 7, false>(sm, base, split, tl); break;
-    case 20: run_passes<D, 8, false>(sm, base, split, tl); break;
-    case 21: run_passes<D, 9, false>(sm, base, split, tl); break;
-    case 22: run_passes<D, 10, false>(sm, base, split, tl); break;
-    default: run_passes<D, 11, false>(sm, base, split, tl); break;
-    }
+    dispatch<D, false>(sm, base, split, tl);
     if (track && tl == len) {
         // snapshot after the whole request: the final state, as stored above
         __syncthreads();
@@ -856,20 +918,130 @@ template <int D> __global__ __launch_bounds__(NT) void prefill_chunked_kernel(Pr
     }
 }
 
-template <int D> hipError_t launch(const PrefillArgs &a, int batch, hipStream_t stream) {
+// Step 1 of a segmented launch: workgroup (segment s, unit) stores dS_s of its
+// column block in workspace slice s.  Segments from the last non-empty one on
+// have nothing to contribute.
+template <int D> __global__ __launch_bounds__(NT) void prefill_delta_kernel(PrefillArgs a) {
+    using G = Geo<D>;
+    __shared__ Smem<D> sm;
+
+    const int H = a.num_heads;
+    const int units = a.pairs * G::NVB;
+    const int seg = static_cast<int>(blockIdx.x) / units;
+    int pair, vb;
+    map_block<G::NVB>(static_cast<int>(blockIdx.x) - seg * units, a.pairs, pair, vb);
+    const int b = pair / H;
+    const int h = pair - b * H;
+    int64_t t0, t1;
+    request_range(a, b, t0, t1);
+    const SegGeom sg = seg_geom(t1 - t0, a.segments);
+    const int slot = a.slot_idx[b];
+    if (slot < 0 || slot >= a.pool_slots || seg >= sg.ne - 1) return;
+    const int hk = h / (H / a.num_kv_heads);
+    float *ds = seg_slice<D>(a, pair, seg);
+    const Job base{a.q, a.k, a.v, a.out, ds, ds,
+                   t0 + static_cast<int64_t>(seg) * sg.cps * C, static_cast<int64_t>(sg.cps) * C,
+                   static_cast<size_t>(H) * D, static_cast<size_t>(h) * D,
+                   static_cast<size_t>(a.num_kv_heads) * D, static_cast<size_t>(hk) * D, vb * VB, a.slopes[h]};
+    dispatch<D, true>(sm, base, nullptr, 0);
+}
+
+// Step 2: workgroup `unit` turns the pool state and dS_0 .. dS_{ne-2} of its
+// column block into the initial states S_0 .. S_{ne-1}, in place (slice s
+// holds dS_s before and S_s after).
+constexpr int kCombineThreads = 256;
+template <int D> __global__ __launch_bounds__(kCombineThreads) void prefill_combine_kernel(PrefillArgs a) {
+    using G = Geo<D>;
+    const int H = a.num_heads;
+    int pair, vb;
+    map_block<G::NVB>(static_cast<int>(blockIdx.x), a.pairs, pair, vb);
+    const int b = pair / H;
+    const int h = pair - b * H;
+    int64_t t0, t1;
+    request_range(a, b, t0, t1);
+    const SegGeom sg = seg_geom(t1 - t0, a.segments);
+    const int slot = a.slot_idx[b];
+    if (slot < 0 || slot >= a.pool_slots || sg.ne == 0) return;
+    const float *state = a.pool + (static_cast<size_t>(slot) * H + h) * (D * D);
+    const float dseg = expf(-a.slopes[h] * static_cast<float>(sg.cps * C));  // e^{-l cps C}
+    float *ws = seg_slice<D>(a, pair, 0);
+    for (int e = threadIdx.x; e < D * VB; e += kCombineThreads) {
+        const int idx = (e / VB) * D + vb * VB + e % VB;
+        float cur = state[idx];
+        for (int s = 0; s < sg.ne; ++s) {
+            float *p = ws + static_cast<size_t>(s) * (D * D) + idx;
+            const float ds = s + 1 < sg.ne ? *p : 0.f;
+            *p = cur;
+            cur = dseg * cur + ds;
+        }
+    }
+}
+
+// Segments for a launch of `units` (request, head, column block) units: as
+// many as fill the GPU's CUs, at most kMaxSegments (or LA_PREFILL_MAX_SEGMENTS
+// when set, 1 turning segments off), each at least kMinSegmentTokens of the
+// longest request.  Snapshot requests are never split.
+constexpr int kMaxSegments = 8;
+constexpr int kMinSegmentTokens = 4096;
+int cu_count() {
+    static int count[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (count[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        count[dev] = n;
+    }
+    return count[dev];
+}
+int choose_segments(int units, int max_seqlen, bool track) {
+    if (track || units <= 0) return 1;
+    int cap = kMaxSegments;
+    if (const char *env = std::getenv("LA_PREFILL_MAX_SEGMENTS")) {
+        const int v = std::atoi(env);
+        cap = v < 1 ? 1 : (v > kMaxSegments ? kMaxSegments : v);
+    }
+    int ns = cu_count() / units;
+    if (ns > cap) ns = cap;
+    if (ns > max_seqlen / kMinSegmentTokens) ns = max_seqlen / kMinSegmentTokens;
+    return ns < 1 ? 1 : ns;
+}
+
+template <int D> hipError_t launch(const PrefillArgs &a, int batch, int max_seqlen, hipStream_t stream) {
     PrefillArgs copy = a;
     copy.pairs = batch * a.num_heads;
+    const unsigned units = static_cast<unsigned>(copy.pairs) * Geo<D>::NVB;
+    copy.segments = choose_segments(static_cast<int>(units), max_seqlen, a.track_lens != nullptr);
+    copy.seg_ws = nullptr;
     void *args[] = {&copy};
-    return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_chunked_kernel<D>),
-                           dim3(static_cast<unsigned>(copy.pairs) * Geo<D>::NVB), dim3(NT), args, 0, stream);
+    if (copy.segments == 1)
+        return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_chunked_kernel<D>), dim3(units), dim3(NT),
+                               args, 0, stream);
+    const size_t ws_bytes = static_cast<size_t>(copy.pairs) * copy.segments * D * D * sizeof(float);
+    void *ws = nullptr;
+    hipError_t e = hipMallocAsync(&ws, ws_bytes, stream);
+    if (e != hipSuccess) return e;
+    copy.seg_ws = static_cast<float *>(ws);
+    e = hipLaunchKernel(reinterpret_cast<const void *>(&prefill_delta_kernel<D>),
+                        dim3(units * (copy.segments - 1)), dim3(NT), args, 0, stream);
+    if (e == hipSuccess)
+        e = hipLaunchKernel(reinterpret_cast<const void *>(&prefill_combine_kernel<D>), dim3(units),
+                            dim3(kCombineThreads), args, 0, stream);
+    if (e == hipSuccess)
+        e = hipLaunchKernel(reinterpret_cast<const void *>(&prefill_chunked_kernel<D>),
+                            dim3(units * copy.segments), dim3(NT), args, 0, stream);
+    const hipError_t f = hipFreeAsync(ws, stream);
+    return e != hipSuccess ? e : f;
 }
 
 }  // namespace
 
-hipError_t launch_prefill_chunked(const PrefillArgs &a, int batch, int head_dim, hipStream_t stream) {
+hipError_t launch_prefill_chunked(const PrefillArgs &a, int batch, int head_dim, int max_seqlen,
+                                  hipStream_t stream) {
     if (batch == 0) return hipSuccess;
-    if (head_dim == 128) return launch<128>(a, batch, stream);
-    if (head_dim == 64) return launch<64>(a, batch, stream);
+    if (head_dim == 128) return launch<128>(a, batch, max_seqlen, stream);
+    if (head_dim == 64) return launch<64>(a, batch, max_seqlen, stream);
     return hipErrorInvalidValue;
 }
 
