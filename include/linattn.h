@@ -109,14 +109,23 @@ la_status la_alibi_slopes(int num_heads, int layer_id, int num_layers, float *sl
  * state_pool[track_slot_idx[b]]; a negative track slot means no snapshot.
  * Track slots must be distinct from each other and from every slot_idx entry.
  *
- * bf16, d = 128: chunked MFMA kernel (fp32 state, bf16 hi/lo operand splits).
- * fp32, or d = 64: token-recurrent fp32 kernel.
+ * bf16 (d = 64 or 128): chunked MFMA kernel (fp32 state, bf16 hi/lo operand
+ * splits).  When its (request, head, 32-column block) units fill only part of
+ * the GPU's compute units and there are no track arrays, every request is split
+ * into up to 8 sequence segments of at least 4096 tokens of the longest
+ * request, run side by side from initial states that a state-only pass and a
+ * combine step compute first (the env var LA_PREFILL_MAX_SEGMENTS caps the
+ * count; 1 turns the split off).  That path allocates a stream-ordered
+ * workspace of batch*H*segments*d*d floats with hipMallocAsync on `stream` and
+ * frees it with hipFreeAsync after the last launch; results agree with the
+ * unsplit call to rounding.
+ * fp32: token-recurrent fp32 kernel.
  * Errors: LA_ERR_INVALID_ARG for NULL pointers (q/k/v/out may be NULL only when
  * total_tokens == 0), negative sizes, num_kv_heads not dividing num_heads,
  * only one of the two track arrays, batch > pool_slots or, with LA_DEBUG=1,
  * inconsistent cu_seqlens/slot_idx/track arrays; LA_ERR_UNSUPPORTED for a
  * head_dim other than 64/128 or an unknown dtype; LA_ERR_HIP on a launch
- * failure.
+ * or workspace allocation failure.
  */
 la_status la_prefill(const void *q, const void *k, const void *v, la_dtype dtype,
                      const int32_t *cu_seqlens, int batch, int64_t total_tokens, int max_seqlen,
