@@ -34,13 +34,17 @@
  *   cu_seqlens     [batch+1] int32, cu_seqlens[0] = 0, non-decreasing,
  *                  cu_seqlens[batch] = total_tokens (packed varlen batch).
  *   slopes         [H] float32 per-head decay rates (see la_alibi_slopes).
+ * q, k, v, out, state_pool, state_out and draft_states must be 16-byte aligned
+ * (the kernels move them with 16-byte vector accesses; a misaligned pointer is
+ * LA_ERR_INVALID_ARG).
  * head_dim (d) is 128 or 64 (the reference's kernels need at least 128 for
  * decode and 64 for prefill, [LA-page] §输入与配置覆盖; both run here on
  * every path).
  *
  * Calls are asynchronous on `stream` (0 = the null stream): the library does
  * no host synchronisation, no device-to-host reads and no allocation on these
- * paths, and keeps no state between calls.  The inputs must not alias out,
+ * paths (except the stream-ordered workspace of a prefill split into sequence
+ * segments, see la_prefill), and keeps no state between calls.  The inputs must not alias out,
  * state_pool or state_out.  Overlapping calls that name the same pool slot race.
  *
  * Errors: every call returns an la_status and never aborts.  Host-visible
@@ -120,8 +124,8 @@ la_status la_alibi_slopes(int num_heads, int layer_id, int num_layers, float *sl
  * frees it with hipFreeAsync after the last launch; results agree with the
  * unsplit call to rounding.
  * fp32: token-recurrent fp32 kernel.
- * Errors: LA_ERR_INVALID_ARG for NULL pointers (q/k/v/out may be NULL only when
- * total_tokens == 0), negative sizes, num_kv_heads not dividing num_heads,
+ * Errors: LA_ERR_INVALID_ARG for NULL or misaligned pointers (q/k/v/out may be
+ * NULL only when total_tokens == 0), negative sizes, num_kv_heads not dividing num_heads,
  * only one of the two track arrays, batch > pool_slots or, with LA_DEBUG=1,
  * inconsistent cu_seqlens/slot_idx/track arrays; LA_ERR_UNSUPPORTED for a
  * head_dim other than 64/128 or an unknown dtype; LA_ERR_HIP on a launch

@@ -75,6 +75,9 @@ la_status debug_check(const int32_t *cu_seqlens, int batch, int64_t total_tokens
     return LA_OK;
 }
 
+// The kernels move q, k, v, out and states with 16-byte vector accesses.
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 la_status common_checks(const void *q, const void *k, const void *v, la_dtype dtype,
                         int64_t total_tokens, int batch, int num_heads, int num_kv_heads,
                         int head_dim, const float *state_pool, int64_t pool_slots,
@@ -88,6 +91,8 @@ la_status common_checks(const void *q, const void *k, const void *v, la_dtype dt
     if (batch > pool_slots) return LA_ERR_INVALID_ARG;  // slots must be distinct
     if (!state_pool || !slopes || (batch > 0 && !slot_idx)) return LA_ERR_INVALID_ARG;
     if (total_tokens > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(state_pool))
+        return LA_ERR_INVALID_ARG;
     if (static_cast<int64_t>(batch) * num_heads * 4 > kMaxGrid) return LA_ERR_INVALID_ARG;
     if (total_tokens > kMaxGrid) return LA_ERR_INVALID_ARG;  // int32 cu_seqlens
     return LA_OK;
@@ -198,6 +203,7 @@ la_status la_verify(const void *q, const void *k, const void *v, la_dtype dtype,
     la_status st = common_checks(q, k, v, dtype, tokens, batch, num_heads, num_kv_heads, head_dim,
                                  state_pool, pool_slots, slot_idx, slopes, out);
     if (st != LA_OK) return st;
+    if (!aligned16(state_out)) return LA_ERR_INVALID_ARG;
     if (debug_mode()) {
         st = debug_check(nullptr, batch, tokens, num_draft, num_draft, slot_idx, pool_slots,
                          nullptr, nullptr, nullptr, stream);
@@ -231,6 +237,7 @@ la_status la_verify_tree(const void *q, const void *k, const void *v, la_dtype d
                                  state_pool, pool_slots, slot_idx, slopes, out);
     if (st != LA_OK) return st;
     if (batch > 0 && !parent_idx) return LA_ERR_INVALID_ARG;
+    if (!aligned16(draft_states)) return LA_ERR_INVALID_ARG;
     if (debug_mode()) {
         st = debug_check(nullptr, batch, tokens, num_draft, num_draft, slot_idx, pool_slots,
                          nullptr, nullptr, parent_idx, stream);

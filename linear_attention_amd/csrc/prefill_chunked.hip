@@ -818,6 +818,7 @@ __device__ __forceinline__ int request_of_rank(const PrefillArgs &a, int batch, 
 // All three read and write the workspace a.seg_ws, [pair][segment][D][D]
 // fp32, in stream order; the pool slot is read by step 2 only and written by
 // step 3 only.
+constexpr int kMaxSegments = 8;  // sequence segments per request, at most
 struct SegGeom {
     int nchunks;  // chunks of the request
     int cps;      // chunks per segment
@@ -948,7 +949,9 @@ template <int D> __global__ __launch_bounds__(NT) void prefill_delta_kernel(Pref
 
 // Step 2: workgroup `unit` turns the pool state and dS_0 .. dS_{ne-2} of its
 // column block into the initial states S_0 .. S_{ne-1}, in place (slice s
-// holds dS_s before and S_s after).
+// holds dS_s before and S_s after).  Each thread owns 4 consecutive columns
+// of 4 rows and loads every dS_s before it runs the chain, so that the loads
+// overlap instead of following one another.
 constexpr int kCombineThreads = 256;
 template <int D> __global__ __launch_bounds__(kCombineThreads) void prefill_combine_kernel(PrefillArgs a) {
     using G = Geo<D>;
@@ -965,14 +968,20 @@ template <int D> __global__ __launch_bounds__(kCombineThreads) void prefill_comb
     const float *state = a.pool + (static_cast<size_t>(slot) * H + h) * (D * D);
     const float dseg = expf(-a.slopes[h] * static_cast<float>(sg.cps * C));  // e^{-l cps C}
     float *ws = seg_slice<D>(a, pair, 0);
-    for (int e = threadIdx.x; e < D * VB; e += kCombineThreads) {
-        const int idx = (e / VB) * D + vb * VB + e % VB;
-        float cur = state[idx];
-        for (int s = 0; s < sg.ne; ++s) {
-            float *p = ws + static_cast<size_t>(s) * (D * D) + idx;
-            const float ds = s + 1 < sg.ne ? *p : 0.f;
-            *p = cur;
-            cur = dseg * cur + ds;
+    constexpr int kQuads = D * VB / 4;  // 4-column groups of the block
+    for (int e = threadIdx.x; e < kQuads; e += kCombineThreads) {
+        const int idx = (e / (VB / 4)) * D + vb * VB + 4 * (e % (VB / 4));
+        f32x4 ds[kMaxSegments];
+#pragma unroll
+        for (int s = 0; s < kMaxSegments; ++s)
+            if (s + 1 < sg.ne) ds[s] = *reinterpret_cast<const f32x4 *>(ws + static_cast<size_t>(s) * (D * D) + idx);
+        f32x4 cur = *reinterpret_cast<const f32x4 *>(state + idx);
+#pragma unroll
+        for (int s = 0; s < kMaxSegments; ++s) {
+            if (s < sg.ne) {
+                *reinterpret_cast<f32x4 *>(ws + static_cast<size_t>(s) * (D * D) + idx) = cur;
+                if (s + 1 < sg.ne) cur = dseg * cur + ds[s];
+            }
         }
     }
 }
@@ -981,7 +990,6 @@ template <int D> __global__ __launch_bounds__(kCombineThreads) void prefill_comb
 // many as fill the GPU's CUs, at most kMaxSegments (or LA_PREFILL_MAX_SEGMENTS
 // when set, 1 turning segments off), each at least kMinSegmentTokens of the
 // longest request.  Snapshot requests are never split.
-constexpr int kMaxSegments = 8;
 constexpr int kMinSegmentTokens = 4096;
 int cu_count() {
     static int count[64];

@@ -105,6 +105,8 @@ def test_prefill_validation(lib):
     assert _prefill(lib, batch=5, P=4) == E   # more requests than distinct slots
     assert _prefill(lib, P=0) == E
     assert _prefill(lib, batch=2 ** 28, P=2 ** 30) == E  # grid too large
+    for name in ("q", "k", "v", "out", "pool"):   # 16-byte vector accesses need aligned pointers
+        assert _prefill(lib, **{name: FAKE + 8}) == E, name
     # empty work returns before any HIP call
     assert _prefill(lib, batch=0, T=0, max_seqlen=0, q=None, k=None, v=None, out=None, cu=FAKE,
                     slot=None) == la.LA_OK
@@ -151,6 +153,8 @@ def test_decode_and_verify_validation(lib):
     assert _verify(lib, batch=-1) == E
     assert _verify(lib, HK=-1) == E
     assert _verify(lib, batch=0, q=None, k=None, v=None, out=None, slot=None) == la.LA_OK
+    assert _decode(lib, pool=FAKE + 4) == E
+    assert _verify(lib, so=FAKE + 2) == E
 
 
 def test_tree_verify_validation(lib):
@@ -163,6 +167,7 @@ def test_tree_verify_validation(lib):
     assert _tree(lib, HK=3) == E
     assert _tree(lib, batch=7, P=4) == E
     assert _tree(lib, batch=-1) == E
+    assert _tree(lib, ds=FAKE + 12) == E
     # draft_states may be NULL, and an empty batch launches nothing
     assert _tree(lib, batch=0, q=None, k=None, v=None, out=None, slot=None, par=None,
                  ds=None) == la.LA_OK
