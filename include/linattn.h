@@ -115,10 +115,10 @@ la_status la_alibi_slopes(int num_heads, int layer_id, int num_layers, float *sl
  *
  * bf16 (d = 64 or 128): chunked MFMA kernel (fp32 state, bf16 hi/lo operand
  * splits).  When its (request, head, 32-column block) units fill only part of
- * the GPU's compute units and there are no track arrays, every request is split
- * into up to 8 sequence segments of at least 4096 tokens of the longest
- * request, run side by side from initial states that a state-only pass and a
- * combine step compute first (the env var LA_PREFILL_MAX_SEGMENTS caps the
+ * the GPU's compute units, the longest request has at least 8192 tokens and
+ * there are no track arrays, every request is split into up to 8 sequence
+ * segments of at least 1024 tokens of the longest request, run side by side
+ * from initial states that a state-only pass and a combine step compute first (the env var LA_PREFILL_MAX_SEGMENTS caps the
  * count; 1 turns the split off).  That path allocates a stream-ordered
  * workspace of batch*H*segments*d*d floats with hipMallocAsync on `stream` and
  * frees it with hipFreeAsync after the last launch; results agree with the
