@@ -109,3 +109,26 @@ def test_out_of_range_slot_in_a_segmented_launch():
     untouched = [s for s in range(wl.pool_slots) if s != wl.slot_idx[0]]
     after = dv["pool"].index_select(0, torch.tensor(untouched, device="cuda")).cpu().numpy()
     assert np.array_equal(after.view(np.uint32), wl.pool[untouched].view(np.uint32)), "state touched"
+
+
+def test_snapshot_request_on_a_splittable_shape():
+    """A long request with few heads would be split, but a snapshot forces the
+    unsplit two-pass path: the track slot gets the state after track_len
+    tokens and the active slot the final state."""
+    wl = W.make("seg-track", "prefill", "bf16", 4, [12345], 3, seed=1207, prefix=[True], slot_idx=[1])
+    tl = 6000
+    log(f"case {wl.name} T={wl.total_tokens} track_len={tl}")
+    dv = device_inputs(wl)
+    out = torch.empty_like(dv["q"])
+    la.la_prefill(dv["q"], dv["k"], dv["v"], dv["cu"], dv["pool"], dv["slot"], dv["slopes"], out, wl.max_seqlen,
+                  track_lens=torch.tensor([tl], dtype=torch.int32, device="cuda"),
+                  track_slot_idx=torch.tensor([0], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    slopes = oracle.alibi_slopes(4, wl.layer_id, wl.num_layers)
+    ref_out, ref_fin, ref_snap = oracle.prefill(wl.q, wl.k, wl.v, wl.cu_seqlens, wl.pool, wl.slot_idx, slopes,
+                                                track_lens=[tl])
+    assert_close(host_io(out), ref_out, TOL["bf16"], f"{wl.name} out")
+    pool = dv["pool"].cpu().numpy()
+    assert_close(pool[1], ref_fin[0], TOL["bf16"], f"{wl.name} final state")
+    assert_close(pool[0], ref_snap[0], TOL["bf16"], f"{wl.name} snapshot")
+    assert np.array_equal(pool[2].view(np.uint32), wl.pool[2].view(np.uint32)), "untouched slot changed"
