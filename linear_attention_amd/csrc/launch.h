@@ -58,7 +58,8 @@ struct PrefillArgs {
     const float *slopes;
     uint16_t *out;
     int segments;   // sequence segments per request (set by the launcher)
-    float *seg_ws;  // their workspace, [batch*H][segments][D][D] fp32
+    int subsegs;    // sub-segments per segment in the state-only pass
+    float *seg_ws;  // their workspace (layout in prefill_chunked.hip)
 };
 // max_seqlen: the longest request (decides how many segments a launch that
 // underfills the GPU splits requests into; any value gives the same results)

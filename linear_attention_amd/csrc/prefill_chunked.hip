@@ -59,6 +59,11 @@
 // Rows past the end of a short last chunk are loaded from the chunk's last
 // row (always in bounds) and given zero weight.
 //
+// Launches with fewer (request, head, column block) units than CUs split
+// their requests into sequence segments that run side by side (see "Sequence
+// segments" below): a full-width state-only pass and a combine step give each
+// segment its initial state first.
+//
 // State tracking ([LA-page] §额外覆盖): a request that snapshots its state
 // after tl tokens runs as two consecutive passes, over [0, tl) and [tl, len);
 // the first pass stores its final state to the track slot and the second
@@ -267,10 +272,10 @@ template <> struct Tiles<3> {
 
 // One chunk for state wave (RH, CH): the inter term of all 64 tokens
 // restricted to its state rows R0..R0+HR-1 (R0 = RH HR) and column tile CH,
-// part[it] (only with kInter), and the update of those rows, S[k][v] = e^{-l c}
-// S + sum_j K[j][k] Vd[j][v].  qdec[it]: weight of the inter term for token
-// i = 16 it + l16 (only without kF); dc: e^{-l c}.
-template <int D, int RH, int CH, bool kF, bool kInter>
+// part[it], and the update of those rows, S[k][v] = e^{-l c} S + sum_j K[j][k]
+// Vd[j][v].  qdec[it]: weight of the inter term for token i = 16 it + l16
+// (only without kF); dc: e^{-l c}.
+template <int D, int RH, int CH, bool kF>
 __device__ __forceinline__ void state_chunk(const uint16_t *sq, const uint16_t *sk, const uint16_t *svh,
                                             const uint16_t *svl, const float (&qdec)[4], float dc, int g,
                                             int l16, f32x4 (&S)[Geo<D>::HMT], f32x4 (&part)[4]) {
@@ -278,45 +283,43 @@ __device__ __forceinline__ void state_chunk(const uint16_t *sq, const uint16_t *
     constexpr int R0 = RH * G::HR;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 
-    if constexpr (kInter) {
-        // Q^T restricted to the wave's rows (B operand of contraction step ks:
-        // lane (g, l16) holds token 16 it + l16 and features R0 + 32ks + 4g + r,
-        // R0 + 32ks + 16 + 4g + r, the order in which the state rows sit in the A
-        // operand below)
-        u16x8 qb[4][G::HKS];
+    // Q^T restricted to the wave's rows (B operand of contraction step ks:
+    // lane (g, l16) holds token 16 it + l16 and features R0 + 32ks + 4g + r,
+    // R0 + 32ks + 16 + 4g + r, the order in which the state rows sit in the A
+    // operand below)
+    u16x8 qb[4][G::HKS];
 #pragma unroll
-        for (int it = 0; it < 4; ++it)
-#pragma unroll
-            for (int ks = 0; ks < G::HKS; ++ks) {
-                const int qr = 16 * it + l16;
-                qb[it][ks] = cat(lds4_single(&sq[q_off<D>(qr, R0 + 32 * ks + 4 * g)]),
-                                 lds4_single(&sq[q_off<D>(qr, R0 + 32 * ks + 16 + 4 * g)]));
-            }
-        // the state as bf16 hi/lo A operand (v x k): for step ks lane (g, l16) holds
-        // rows R0 + 32ks + 4g + r (tile 2ks) and R0 + 32ks + 16 + 4g + r (tile
-        // 2ks + 1) of column v = 16 CH + l16
-        u16x8 sa_hi[G::HKS], sa_lo[G::HKS];
+    for (int it = 0; it < 4; ++it)
 #pragma unroll
         for (int ks = 0; ks < G::HKS; ++ks) {
-            u16x4 h0, l0, h1, l1;
-            split4(S[2 * ks], h0, l0);
-            split4(S[2 * ks + 1], h1, l1);
-            sa_hi[ks] = cat(h0, h1);
-            sa_lo[ks] = cat(l0, l1);
+            const int qr = 16 * it + l16;
+            qb[it][ks] = cat(lds4_single(&sq[q_off<D>(qr, R0 + 32 * ks + 4 * g)]),
+                             lds4_single(&sq[q_off<D>(qr, R0 + 32 * ks + 16 + 4 * g)]));
         }
-        __builtin_amdgcn_sched_barrier(0);
+    // the state as bf16 hi/lo A operand (v x k): for step ks lane (g, l16) holds
+    // rows R0 + 32ks + 4g + r (tile 2ks) and R0 + 32ks + 16 + 4g + r (tile
+    // 2ks + 1) of column v = 16 CH + l16
+    u16x8 sa_hi[G::HKS], sa_lo[G::HKS];
+#pragma unroll
+    for (int ks = 0; ks < G::HKS; ++ks) {
+        u16x4 h0, l0, h1, l1;
+        split4(S[2 * ks], h0, l0);
+        split4(S[2 * ks + 1], h1, l1);
+        sa_hi[ks] = cat(h0, h1);
+        sa_lo[ks] = cat(l0, l1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
-        // inter term O^T[v][i] = sum_k S^T[v][k] Q^T[k][i] over the wave's rows
+    // inter term O^T[v][i] = sum_k S^T[v][k] Q^T[k][i] over the wave's rows
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            f32x4 acc = z;
+    for (int it = 0; it < 4; ++it) {
+        f32x4 acc = z;
 #pragma unroll
-            for (int ks = 0; ks < G::HKS; ++ks) {
-                acc = mma(sa_hi[ks], qb[it][ks], acc);
-                acc = mma(sa_lo[ks], qb[it][ks], acc);
-            }
-            part[it] = kF ? acc : acc * qdec[it];
+        for (int ks = 0; ks < G::HKS; ++ks) {
+            acc = mma(sa_hi[ks], qb[it][ks], acc);
+            acc = mma(sa_lo[ks], qb[it][ks], acc);
         }
+        part[it] = kF ? acc : acc * qdec[it];
     }
     // fragments of the update: K^T rows of the wave and its column tile of the
     // decayed V, with tokens along the contraction
@@ -473,9 +476,7 @@ struct Job {
 //     decays the V of chunk ci + 1.
 // Partials, decayed V and the Q/K tiles are double-buffered by chunk parity,
 // V is a 3-slot ring, so nothing written in one interval is read in it.
-// With kDelta the pass computes the state only: no Q tiles, no scores, no
-// inter term and no output, with the same chunk loop and barriers.
-template <int D, int W, bool kF, bool kDelta>
+template <int D, int W, bool kF>
 __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
     using G = Geo<D>;
     constexpr bool kState = W < 4;
@@ -513,8 +514,7 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
         for (int mt = 0; mt < G::HMT; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                S[mt][r] = kDelta ? 0.f
-                                  : sigma * jb.state_in[(RH * G::HR + 16 * mt + 4 * g + r) * D + col0 + 16 * CH + l16];
+                S[mt][r] = sigma * jb.state_in[(RH * G::HR + 16 * mt + 4 * g + r) * D + col0 + 16 * CH + l16];
 #pragma unroll
         for (int it = 0; it < 4; ++it) qdec[it] = expf(-lam * static_cast<float>(16 * it + l16 + 1));
         // output factor of the stored row blocks (token i = 16B + l16)
@@ -573,7 +573,7 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
 #pragma unroll
         for (int u = 0; u < QPW; ++u) {
             const uint32_t r = static_cast<uint32_t>(qk_row[u] < c ? qk_row[u] : c - 1);
-            if constexpr (!kDelta) rq[u] = *reinterpret_cast<const u16x8 *>(qb + (r * row + 8 * q_unit[u]));
+            rq[u] = *reinterpret_cast<const u16x8 *>(qb + (r * row + 8 * q_unit[u]));
             rk[u] = *reinterpret_cast<const u16x8 *>(kb + (r * kvrow + 8 * k_unit[u]));
         }
         if (n + 1 < nchunks) load_v(n + 1);
@@ -584,7 +584,7 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
 #pragma unroll
         for (int u = 0; u < QPW; ++u) {
             const int dst = 512 * (HI * QPW + u) + 8 * lane;
-            if constexpr (!kDelta) *reinterpret_cast<u16x8 *>(&sm.q[buf][dst]) = rq[u];
+            *reinterpret_cast<u16x8 *>(&sm.q[buf][dst]) = rq[u];
             *reinterpret_cast<u16x8 *>(&sm.k[buf][dst]) = rk[u];
         }
         if (n + 1 < nchunks) store_v(n + 1);
@@ -678,20 +678,18 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
         }
         const int buf = ci & 1;
         if constexpr (kState) {
-            if (!kDelta && ci > 0) finalize(ci - 1);
+            if (ci > 0) finalize(ci - 1);
             f32x4 part[4];
-            state_chunk<D, RH, CH, kF, !kDelta>(sm.q[buf], sm.k[buf], sm.vd_hi[buf], sm.vd_lo[buf], qdec,
-                                                last ? dc_last : dc_full, g, l16, S, part);
+            state_chunk<D, RH, CH, kF>(sm.q[buf], sm.k[buf], sm.vd_hi[buf], sm.vd_lo[buf], qdec,
+                                       last ? dc_last : dc_full, g, l16, S, part);
             // row blocks of the partner to the partner, the own ones kept
-            if constexpr (!kDelta) {
 #pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    sm.inter[buf][R][m][lane] = part[2 * (1 - RH) + m];
-                    keep[m] = part[2 * RH + m];
-                }
+            for (int m = 0; m < 2; ++m) {
+                sm.inter[buf][R][m][lane] = part[2 * (1 - RH) + m];
+                keep[m] = part[2 * RH + m];
             }
         }
-        if constexpr (kScore && !kDelta) {
+        if constexpr (kScore) {
             if (last && c_last != C && nchunks > 1) score_weights<R, kF>(lam, g, l16, c_last, mdec);
             f32x4 ipart[2][2];
             score_chunk<D, R, kF>(sm.q[buf], sm.k[buf], sm.v[ci % 3], mdec, g, l16, ipart);
@@ -703,7 +701,7 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
     }
     lds_barrier();  // the partials of the last chunk are in LDS
     if constexpr (kState) {
-        if constexpr (!kDelta) finalize(nchunks - 1);
+        finalize(nchunks - 1);
         const float unscale = kF ? expf(32.f * lam) : 1.f;
 #pragma unroll
         for (int mt = 0; mt < G::HMT; ++mt)
@@ -715,10 +713,10 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
 
 // The passes of wave W over a request: one over [0, len), or with a snapshot
 // inside the request [0, tl) into the track slot and then [tl, len) from it.
-template <int D, int W, bool kF, bool kDelta>
+template <int D, int W, bool kF>
 __device__ __forceinline__ void run_passes(Smem<D> &sm, const Job &base, float *track, int64_t tl) {
     if (!track) {
-        run_wave<D, W, kF, kDelta>(sm, base);
+        run_wave<D, W, kF>(sm, base);
         return;
     }
     for (int i = 0; i < 2; ++i) {
@@ -727,41 +725,41 @@ __device__ __forceinline__ void run_passes(Smem<D> &sm, const Job &base, float *
         jb.len = i == 0 ? tl : base.len - tl;
         jb.state_in = i == 0 ? base.state_in : track;
         jb.state_out = i == 0 ? track : base.state_out;
-        run_wave<D, W, kF, kDelta>(sm, jb);
+        run_wave<D, W, kF>(sm, jb);
     }
 }
 
 // The wave's role and decay path for one pass: wave index and, for slopes
 // outside [0, 2], the explicit (not factored) decay.  Slopes in [0, 2] take
 // the factored path (the largest ALiBi slope is below 1).
-template <int D, bool kDelta>
+template <int D>
 __device__ __forceinline__ void dispatch(Smem<D> &sm, const Job &base, float *split, int64_t tl) {
     const bool factored = base.lam >= 0.f && base.lam <= 2.f;
     switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) + (factored ? 0 : 12)) {
-    case 0: run_passes<D, 0, true, kDelta>(sm, base, split, tl); break;
-    case 1: run_passes<D, 1, true, kDelta>(sm, base, split, tl); break;
-    case 2: run_passes<D, 2, true, kDelta>(sm, base, split, tl); break;
-    case 3: run_passes<D, 3, true, kDelta>(sm, base, split, tl); break;
-    case 4: run_passes<D, 4, true, kDelta>(sm, base, split, tl); break;
-    case 5: run_passes<D, 5, true, kDelta>(sm, base, split, tl); break;
-    case 6: run_passes<D, 6, true, kDelta>(sm, base, split, tl); break;
-    case 7: run_passes<D, 7, true, kDelta>(sm, base, split, tl); break;
-    case 8: run_passes<D, 8, true, kDelta>(sm, base, split, tl); break;
-    case 9: run_passes<D, 9, true, kDelta>(sm, base, split, tl); break;
-    case 10: run_passes<D, 10, true, kDelta>(sm, base, split, tl); break;
-    case 11: run_passes<D, 11, true, kDelta>(sm, base, split, tl); break;
-    case 12: run_passes<D, 0, false, kDelta>(sm, base, split, tl); break;
-    case 13: run_passes<D, 1, false, kDelta>(sm, base, split, tl); break;
-    case 14: run_passes<D, 2, false, kDelta>(sm, base, split, tl); break;
-    case 15: run_passes<D, 3, false, kDelta>(sm, base, split, tl); break;
-    case 16: run_passes<D, 4, false, kDelta>(sm, base, split, tl); break;
-    case 17: run_passes<D, 5, false, kDelta>(sm, base, split, tl); break;
-    case 18: run_passes<D, 6, false, kDelta>(sm, base, split, tl); break;
-    case 19: run_passes<D, 7, false, kDelta>(sm, base, split, tl); break;
-    case 20: run_passes<D, 8, false, kDelta>(sm, base, split, tl); break;
-    case 21: run_passes<D, 9, false, kDelta>(sm, base, split, tl); break;
-    case 22: run_passes<D, 10, false, kDelta>(sm, base, split, tl); break;
-    default: run_passes<D, 11, false, kDelta>(sm, base, split, tl); break;
+    case 0: run_passes<D, 0, true>(sm, base, split, tl); break;
+    case 1: run_passes<D, 1, true>(sm, base, split, tl); break;
+    case 2: run_passes<D, 2, true>(sm, base, split, tl); break;
+    case 3: run_passes<D, 3, true>(sm, base, split, tl); break;
+    case 4: run_passes<D, 4, true>(sm, base, split, tl); break;
+    case 5: run_passes<D, 5, true>(sm, base, split, tl); break;
+    case 6: run_passes<D, 6, true>(sm, base, split, tl); break;
+    case 7: run_passes<D, 7, true>(sm, base, split, tl); break;
+    case 8: run_passes<D, 8, true>(sm, base, split, tl); break;
+    case 9: run_passes<D, 9, true>(sm, base, split, tl); break;
+    case 10: run_passes<D, 10, true>(sm, base, split, tl); break;
+    case 11: run_passes<D, 11, true>(sm, base, split, tl); break;
+    case 12: run_passes<D, 0, false>(sm, base, split, tl); break;
+    case 13: run_passes<D, 1, false>(sm, base, split, tl); break;
+    case 14: run_passes<D, 2, false>(sm, base, split, tl); break;
+    case 15: run_passes<D, 3, false>(sm, base, split, tl); break;
+    case 16: run_passes<D, 4, false>(sm, base, split, tl); break;
+    case 17: run_passes<D, 5, false>(sm, base, split, tl); break;
+    case 18: run_passes<D, 6, false>(sm, base, split, tl); break;
+    case 19: run_passes<D, 7, false>(sm, base, split, tl); break;
+    case 20: run_passes<D, 8, false>(sm, base, split, tl); break;
+    case 21: run_passes<D, 9, false>(sm, base, split, tl); break;
+    case 22: run_passes<D, 10, false>(sm, base, split, tl); break;
+    default: run_passes<D, 11, false>(sm, base, split, tl); break;
     }
 }
 
@@ -807,17 +805,16 @@ __device__ __forceinline__ int request_of_rank(const PrefillArgs &a, int batch, 
 // Sequence segments.  A launch whose (request, head, column block) units
 // fill only part of the GPU splits every request into up to a.segments
 // segments of whole chunks, cps chunks each, and runs them side by side:
-//   1. prefill_delta_kernel: the state contribution of every segment but the
-//      last, dS_s = sum over its tokens t of e^{-l(end_s - 1 - t)} k_t v_t^T
-//      (the recurrence from a zero state, no outputs);
+//   1. prefill_delta_full_kernel: the state contribution of every segment but
+//      the last, in sub-segments of whole chunks: dS_{s,q} = sum over the
+//      tokens t of sub-segment q of e^{-l(end_q - 1 - t)} k_t v_t^T (the
+//      recurrence from a zero state, no outputs);
 //   2. prefill_combine_kernel: the state before each segment, by the same
-//      recurrence at segment granularity: S_0 is the pool state and
-//      S_{s+1} = e^{-l cps C} S_s + dS_s;
+//      recurrence at sub-segment granularity from the pool state S_0;
 //   3. prefill_chunked_kernel: every segment from its own initial state, as a
 //      request of its own; the last segment stores the final state.
-// All three read and write the workspace a.seg_ws, [pair][segment][D][D]
-// fp32, in stream order; the pool slot is read by step 2 only and written by
-// step 3 only.
+// All three use the workspace a.seg_ws in stream order; the pool slot is read
+// by step 2 only and written by step 3 only.
 constexpr int kMaxSegments = 8;  // sequence segments per request, at most
 struct SegGeom {
     int nchunks;  // chunks of the request
@@ -831,8 +828,21 @@ __device__ __forceinline__ SegGeom seg_geom(int64_t len, int segments) {
     g.ne = g.cps > 0 ? (g.nchunks + g.cps - 1) / g.cps : 0;
     return g;
 }
+// Workspace a.seg_ws: the contributions dS_{s,q} of sub-segment q of segment s,
+// [pair][segments - 1][subsegs][D][D], then the initial states S_s,
+// [pair][segments][D][D], fp32.
+template <int D> __device__ __forceinline__ float *ds_slice(const PrefillArgs &a, int pair, int s, int q) {
+    return a.seg_ws + ((static_cast<size_t>(pair) * (a.segments - 1) + s) * a.subsegs + q) * (D * D);
+}
 template <int D> __device__ __forceinline__ float *seg_slice(const PrefillArgs &a, int pair, int s) {
-    return a.seg_ws + (static_cast<size_t>(pair) * a.segments + s) * (D * D);
+    return a.seg_ws + (static_cast<size_t>(a.pairs) * (a.segments - 1) * a.subsegs +
+                       static_cast<size_t>(pair) * a.segments + s) * (D * D);
+}
+// Sub-segment q of a segment of cps chunks: chunks [c0, c0 + n) of it.
+__device__ __forceinline__ void subseg_range(int cps, int subsegs, int q, int &c0, int &n) {
+    const int spc = (cps + subsegs - 1) / subsegs;
+    c0 = q * spc;
+    n = c0 >= cps ? 0 : (cps - c0 < spc ? cps - c0 : spc);
 }
 
 template <int D> __global__ __launch_bounds__(NT) void prefill_chunked_kernel(PrefillArgs a) {
@@ -908,7 +918,7 @@ template <int D> __global__ __launch_bounds__(NT) void prefill_chunked_kernel(Pr
                    static_cast<size_t>(a.num_kv_heads) * D, static_cast<size_t>(hk) * D, col0, a.slopes[h]};
     // a snapshot strictly inside the request splits it into two passes
     float *split = track && tl > 0 && tl < len ? track : nullptr;
-    dispatch<D, false>(sm, base, split, tl);
+    dispatch<D>(sm, base, split, tl);
     if (track && tl == len) {
         // snapshot after the whole request: the final state, as stored above
         __syncthreads();
@@ -919,18 +929,161 @@ template <int D> __global__ __launch_bounds__(NT) void prefill_chunked_kernel(Pr
     }
 }
 
-// Step 1 of a segmented launch: workgroup (segment s, unit) stores dS_s of its
-// column block in workspace slice s.  Segments from the last non-empty one on
-// have nothing to contribute.
-template <int D> __global__ __launch_bounds__(NT) void prefill_delta_kernel(PrefillArgs a) {
-    using G = Geo<D>;
-    __shared__ Smem<D> sm;
+// Step 1, full width: workgroup (pair, segment s, sub-segment q) keeps the
+// whole D x D contribution of its sub-segment, so each chunk's K is loaded
+// once and not once per column block.  All chunks of a non-final segment are
+// full.  Eight waves: update wave W (0..3) holds value columns
+// W*D/4 .. W*D/4 + D/4 - 1 of all D rows in MFMA accumulators; staging wave R
+// (4..7) moves token rows 16(R-4) .. 16(R-4) + 15 of every chunk, two chunks
+// ahead, and writes K and the decayed V (e^{-l(C - 1 - j)} v_j, split hi + lo)
+// to LDS, double-buffered by chunk parity, one barrier per chunk.
+constexpr int kDeltaWaves = 8;
+template <int D> struct DeltaSmem {
+    uint16_t k[2][C * D];   // K, token-major, K-tile swizzle
+    uint16_t vh[2][C * D];  // decayed V, hi and lo, same layout
+    uint16_t vl[2][C * D];
+};
 
+template <int D, int W>
+__device__ __forceinline__ void delta_wave(DeltaSmem<D> &sm, const uint16_t *kb, const uint16_t *vb, size_t kvrow,
+                                           int nchunks, float lam, float *out) {
+    using G = Geo<D>;
+    constexpr bool kStage = W >= 4;
+    const int lane = threadIdx.x & 63;
+    const int l16 = lane & 15, g = lane >> 4;
+
+    // ---- update waves
+    constexpr int MT = D / 16;   // row tiles
+    constexpr int NTW = D / 64;  // column tiles per wave
+    f32x4 acc[MT][NTW];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int n = 0; n < NTW; ++n) acc[mt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const float dc = expf(-lam * static_cast<float>(C));
+    auto update = [&](int buf) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int n = 0; n < NTW; ++n) acc[mt][n] *= dc;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            u16x8 ka[MT], bh[NTW], bl[NTW];
+#pragma unroll
+            for (int n = 0; n < NTW; ++n) {
+                const int c0 = 16 * ((W & 3) * NTW + n);
+                bh[n] = cat(ldtr_k<D>(sm.vh[buf], 32 * s2, c0, g, l16), ldtr_k<D>(sm.vh[buf], 32 * s2 + 16, c0, g, l16));
+                bl[n] = cat(ldtr_k<D>(sm.vl[buf], 32 * s2, c0, g, l16), ldtr_k<D>(sm.vl[buf], 32 * s2 + 16, c0, g, l16));
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+                ka[mt] = cat(ldtr_k<D>(sm.k[buf], 32 * s2, 16 * mt, g, l16),
+                             ldtr_k<D>(sm.k[buf], 32 * s2 + 16, 16 * mt, g, l16));
+            lds_wait();
+#pragma unroll
+            for (int n = 0; n < NTW; ++n) {
+                pin(bh[n]);
+                pin(bl[n]);
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) pin(ka[mt]);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+                for (int n = 0; n < NTW; ++n) {
+                    acc[mt][n] = mma(ka[mt], bh[n], acc[mt][n]);
+                    acc[mt][n] = mma(ka[mt], bl[n], acc[mt][n]);
+                }
+        }
+    };
+
+    // ---- staging waves: 16 token rows of K and of V per chunk, KB blocks of 1 KB each
+    constexpr int KB = D / 32;
+    const int R = (W & 3);
+    int row[KB], unit[KB];
+    float wv[KB];
+#pragma unroll
+    for (int b = 0; b < KB; ++b) {
+        row[b] = 16 * R + G::RPB * b + lane / G::UPR;
+        unit[b] = (lane % G::UPR) ^ swz_k<D>(row[b]);
+        wv[b] = expf(-lam * static_cast<float>(C - 1 - row[b]));
+    }
+    u16x8 rk[2][KB], rv[2][KB];
+    auto load = [&](int n0, int set) {  // chunks past the end reload the last one
+        const int n = n0 < nchunks ? n0 : nchunks - 1;
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+            const size_t off = (static_cast<size_t>(n) * C + row[b]) * kvrow + 8 * unit[b];
+            rk[set][b] = *reinterpret_cast<const u16x8 *>(kb + off);
+            rv[set][b] = *reinterpret_cast<const u16x8 *>(vb + off);
+        }
+    };
+    auto store = [&](int n, int set) {
+        const int buf = n & 1;
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+            const int dst = 512 * (R * KB + b) + 8 * lane;
+            *reinterpret_cast<u16x8 *>(&sm.k[buf][dst]) = rk[set][b];
+            f32x4 x0, x1;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x0[e] = bf16_to_f32(rv[set][b][e]) * wv[b];
+                x1[e] = bf16_to_f32(rv[set][b][4 + e]) * wv[b];
+            }
+            u16x4 h0, l0, h1, l1;
+            split4(x0, h0, l0);
+            split4(x1, h1, l1);
+            *reinterpret_cast<u16x8 *>(&sm.vh[buf][dst]) = cat(h0, h1);
+            *reinterpret_cast<u16x8 *>(&sm.vl[buf][dst]) = cat(l0, l1);
+        }
+    };
+
+    if constexpr (kStage) {
+        load(0, 0);
+        store(0, 0);
+        load(1, 1);
+        load(2, 0);
+    }
+    __syncthreads();
+    // chunk ci: the staging waves write chunk ci + 1 (register set (ci + 1) % 2)
+    // and load chunk ci + 3 into the same set; the loop runs two chunks per
+    // iteration so that the set is a constant and every path issues the same
+    // loads (exact wait counts)
+    auto step = [&](int ci, int set) {
+        lds_barrier();
+        if constexpr (kStage) {
+            if (ci + 1 < nchunks) store(ci + 1, set);
+            load(ci + 3, set);
+        } else {
+            update(ci & 1);
+        }
+    };
+    int ci = 0;
+    for (; ci + 1 < nchunks; ci += 2) {
+        step(ci, 1);
+        step(ci + 1, 0);
+    }
+    if (ci < nchunks) step(ci, 1);
+    if constexpr (kStage) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the loads past the end
+    } else {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    out[(16 * mt + 4 * g + r) * D + 16 * ((W & 3) * NTW + n) + l16] = acc[mt][n][r];
+    }
+}
+
+template <int D> __global__ __launch_bounds__(64 * kDeltaWaves) void prefill_delta_full_kernel(PrefillArgs a) {
+    __shared__ DeltaSmem<D> sm;
     const int H = a.num_heads;
-    const int units = a.pairs * G::NVB;
-    const int seg = static_cast<int>(blockIdx.x) / units;
-    int pair, vb;
-    map_block<G::NVB>(static_cast<int>(blockIdx.x) - seg * units, a.pairs, pair, vb);
+    const int per_pair = (a.segments - 1) * a.subsegs;
+    const int pair = static_cast<int>(blockIdx.x) / per_pair;
+    const int rest = static_cast<int>(blockIdx.x) - pair * per_pair;
+    const int seg = rest / a.subsegs, q = rest - seg * a.subsegs;
     const int b = pair / H;
     const int h = pair - b * H;
     int64_t t0, t1;
@@ -938,21 +1091,34 @@ template <int D> __global__ __launch_bounds__(NT) void prefill_delta_kernel(Pref
     const SegGeom sg = seg_geom(t1 - t0, a.segments);
     const int slot = a.slot_idx[b];
     if (slot < 0 || slot >= a.pool_slots || seg >= sg.ne - 1) return;
+    int c0, nch;
+    subseg_range(sg.cps, a.subsegs, q, c0, nch);
+    if (nch == 0) return;
     const int hk = h / (H / a.num_kv_heads);
-    float *ds = seg_slice<D>(a, pair, seg);
-    const Job base{a.q, a.k, a.v, a.out, ds, ds,
-                   t0 + static_cast<int64_t>(seg) * sg.cps * C, static_cast<int64_t>(sg.cps) * C,
-                   static_cast<size_t>(H) * D, static_cast<size_t>(h) * D,
-                   static_cast<size_t>(a.num_kv_heads) * D, static_cast<size_t>(hk) * D, vb * VB, a.slopes[h]};
-    dispatch<D, true>(sm, base, nullptr, 0);
+    const size_t kvrow = static_cast<size_t>(a.num_kv_heads) * D;
+    const int64_t tstart = t0 + (static_cast<int64_t>(seg) * sg.cps + c0) * C;
+    const size_t base = static_cast<size_t>(tstart) * kvrow + static_cast<size_t>(hk) * D;
+    float *out = ds_slice<D>(a, pair, seg, q);
+    const float lam = a.slopes[h];
+    switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
+    case 0: delta_wave<D, 0>(sm, a.k + base, a.v + base, kvrow, nch, lam, out); break;
+    case 1: delta_wave<D, 1>(sm, a.k + base, a.v + base, kvrow, nch, lam, out); break;
+    case 2: delta_wave<D, 2>(sm, a.k + base, a.v + base, kvrow, nch, lam, out); break;
+    case 3: delta_wave<D, 3>(sm, a.k + base, a.v + base, kvrow, nch, lam, out); break;
+    case 4: delta_wave<D, 4>(sm, a.k + base, a.v + base, kvrow, nch, lam, out); break;
+    case 5: delta_wave<D, 5>(sm, a.k + base, a.v + base, kvrow, nch, lam, out); break;
+    case 6: delta_wave<D, 6>(sm, a.k + base, a.v + base, kvrow, nch, lam, out); break;
+    default: delta_wave<D, 7>(sm, a.k + base, a.v + base, kvrow, nch, lam, out); break;
+    }
 }
 
-// Step 2: workgroup `unit` turns the pool state and dS_0 .. dS_{ne-2} of its
-// column block into the initial states S_0 .. S_{ne-1}, in place (slice s
-// holds dS_s before and S_s after).  Each thread owns 4 consecutive columns
-// of 4 rows and loads every dS_s before it runs the chain, so that the loads
-// overlap instead of following one another.
+// Step 2: workgroup `unit` turns the pool state and the sub-segment
+// contributions of its column block into the initial states S_0 .. S_{ne-1}:
+// S_{s+1} is S_s carried through the sub-segments q of segment s,
+// S <- e^{-l n_q C} S + dS_{s,q}.  Each thread owns 4 consecutive columns of
+// some rows and loads every dS it needs before it runs the chain.
 constexpr int kCombineThreads = 256;
+constexpr int kMaxSubsegs = 4;
 template <int D> __global__ __launch_bounds__(kCombineThreads) void prefill_combine_kernel(PrefillArgs a) {
     using G = Geo<D>;
     const int H = a.num_heads;
@@ -966,21 +1132,36 @@ template <int D> __global__ __launch_bounds__(kCombineThreads) void prefill_comb
     const int slot = a.slot_idx[b];
     if (slot < 0 || slot >= a.pool_slots || sg.ne == 0) return;
     const float *state = a.pool + (static_cast<size_t>(slot) * H + h) * (D * D);
-    const float dseg = expf(-a.slopes[h] * static_cast<float>(sg.cps * C));  // e^{-l cps C}
-    float *ws = seg_slice<D>(a, pair, 0);
+    const float lam = a.slopes[h];
+    float dq[kMaxSubsegs];  // decay over each sub-segment (0: empty)
+    int nq[kMaxSubsegs];
+#pragma unroll
+    for (int q = 0; q < kMaxSubsegs; ++q) {
+        int c0 = 0, n = 0;
+        if (q < a.subsegs) subseg_range(sg.cps, a.subsegs, q, c0, n);
+        nq[q] = n;
+        dq[q] = expf(-lam * static_cast<float>(n * C));
+    }
     constexpr int kQuads = D * VB / 4;  // 4-column groups of the block
     for (int e = threadIdx.x; e < kQuads; e += kCombineThreads) {
         const int idx = (e / (VB / 4)) * D + vb * VB + 4 * (e % (VB / 4));
-        f32x4 ds[kMaxSegments];
+        f32x4 ds[kMaxSegments - 1][kMaxSubsegs];
 #pragma unroll
-        for (int s = 0; s < kMaxSegments; ++s)
-            if (s + 1 < sg.ne) ds[s] = *reinterpret_cast<const f32x4 *>(ws + static_cast<size_t>(s) * (D * D) + idx);
+        for (int s = 0; s < kMaxSegments - 1; ++s)
+#pragma unroll
+            for (int q = 0; q < kMaxSubsegs; ++q)
+                if (s + 1 < sg.ne && nq[q] > 0)
+                    ds[s][q] = *reinterpret_cast<const f32x4 *>(ds_slice<D>(a, pair, s, q) + idx);
         f32x4 cur = *reinterpret_cast<const f32x4 *>(state + idx);
 #pragma unroll
         for (int s = 0; s < kMaxSegments; ++s) {
             if (s < sg.ne) {
-                *reinterpret_cast<f32x4 *>(ws + static_cast<size_t>(s) * (D * D) + idx) = cur;
-                if (s + 1 < sg.ne) cur = dseg * cur + ds[s];
+                *reinterpret_cast<f32x4 *>(seg_slice<D>(a, pair, s) + idx) = cur;
+                if (s + 1 < sg.ne) {
+#pragma unroll
+                    for (int q = 0; q < kMaxSubsegs; ++q)
+                        if (nq[q] > 0) cur = dq[q] * cur + ds[s][q];
+                }
             }
         }
     }
@@ -1031,13 +1212,17 @@ template <int D> hipError_t launch(const PrefillArgs &a, int batch, int max_seql
     if (copy.segments == 1)
         return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_chunked_kernel<D>), dim3(units), dim3(NT),
                                args, 0, stream);
-    const size_t ws_bytes = static_cast<size_t>(copy.pairs) * copy.segments * D * D * sizeof(float);
+    // sub-segments: enough state-only workgroups to fill the CUs
+    const int per = copy.pairs * (copy.segments - 1);
+    int sub = cu_count() / per;
+    copy.subsegs = sub < 1 ? 1 : (sub > kMaxSubsegs ? kMaxSubsegs : sub);
+    const size_t slices = static_cast<size_t>(per) * copy.subsegs + static_cast<size_t>(copy.pairs) * copy.segments;
     void *ws = nullptr;
-    hipError_t e = hipMallocAsync(&ws, ws_bytes, stream);
+    hipError_t e = hipMallocAsync(&ws, slices * D * D * sizeof(float), stream);
     if (e != hipSuccess) return e;
     copy.seg_ws = static_cast<float *>(ws);
-    e = hipLaunchKernel(reinterpret_cast<const void *>(&prefill_delta_kernel<D>),
-                        dim3(units * (copy.segments - 1)), dim3(NT), args, 0, stream);
+    e = hipLaunchKernel(reinterpret_cast<const void *>(&prefill_delta_full_kernel<D>),
+                        dim3(static_cast<unsigned>(per * copy.subsegs)), dim3(64 * kDeltaWaves), args, 0, stream);
     if (e == hipSuccess)
         e = hipLaunchKernel(reinterpret_cast<const void *>(&prefill_combine_kernel<D>), dim3(units),
                             dim3(kCombineThreads), args, 0, stream);
