@@ -121,15 +121,15 @@ la_status la_alibi_slopes(int num_heads, int layer_id, int num_layers, float *sl
  * from initial states that a state-only pass and a combine step compute first (the env var LA_PREFILL_MAX_SEGMENTS caps the
  * count; 1 turns the split off).  That path allocates a stream-ordered
  * workspace of batch*H*segments*d*d floats with hipMallocAsync on `stream` and
- * frees it with hipFreeAsync after the last launch; results agree with the
- * unsplit call to rounding.
+ * frees it with hipFreeAsync after the last launch (if that allocation fails
+ * the call runs unsplit); results agree with the unsplit call to rounding.
  * fp32: token-recurrent fp32 kernel.
  * Errors: LA_ERR_INVALID_ARG for NULL or misaligned pointers (q/k/v/out may be
  * NULL only when total_tokens == 0), negative sizes, num_kv_heads not dividing num_heads,
  * only one of the two track arrays, batch > pool_slots or, with LA_DEBUG=1,
  * inconsistent cu_seqlens/slot_idx/track arrays; LA_ERR_UNSUPPORTED for a
  * head_dim other than 64/128 or an unknown dtype; LA_ERR_HIP on a launch
- * or workspace allocation failure.
+ * failure.
  */
 la_status la_prefill(const void *q, const void *k, const void *v, la_dtype dtype,
                      const int32_t *cu_seqlens, int batch, int64_t total_tokens, int max_seqlen,

@@ -1219,7 +1219,13 @@ template <int D> hipError_t launch(const PrefillArgs &a, int batch, int max_seql
     const size_t slices = static_cast<size_t>(per) * copy.subsegs + static_cast<size_t>(copy.pairs) * copy.segments;
     void *ws = nullptr;
     hipError_t e = hipMallocAsync(&ws, slices * D * D * sizeof(float), stream);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess) {
+        // no workspace (out of memory, no stream-ordered pool): run unsplit
+        (void)hipGetLastError();
+        copy.segments = 1;
+        return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_chunked_kernel<D>), dim3(units), dim3(NT),
+                               args, 0, stream);
+    }
     copy.seg_ws = static_cast<float *>(ws);
     e = hipLaunchKernel(reinterpret_cast<const void *>(&prefill_delta_full_kernel<D>),
                         dim3(static_cast<unsigned>(per * copy.subsegs)), dim3(64 * kDeltaWaves), args, 0, stream);
