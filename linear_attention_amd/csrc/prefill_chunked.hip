@@ -182,15 +182,6 @@ __device__ __forceinline__ u16x4 tr_at(const uint16_t *p) {
     asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
     return __builtin_bit_cast(u16x4, r);
 }
-// The same read at a byte offset fixed at compile time (the instruction's
-// 16-bit offset field), so that reads a constant distance apart share one
-// address register.
-template <int OFF> __device__ __forceinline__ u16x4 tr_off(uint32_t addr) {
-    static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
-    uint64_t r;
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF));
-    return __builtin_bit_cast(u16x4, r);
-}
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void pin(u16x8 &x) { asm volatile("" : "+v"(x)); }
 template <int D>
@@ -1121,403 +1112,6 @@ template <int D> __global__ __launch_bounds__(64 * kDeltaWaves) void prefill_del
     }
 }
 
-// ---------------------------------------------------------------------------
-// Full-width prefill (D = 128): one workgroup per (request, head, segment)
-// keeps the whole 128 x 128 state, so Q and K are staged once per head and
-// the 10 score tiles are computed once, and every output is finished by the
-// wave that owns its columns (no partial sums through LDS).  Eight waves,
-// two per SIMD:
-//   * state wave w (0..3) keeps all 128 rows of value columns 32w .. 32w + 31
-//     (64 accumulator registers); per chunk it computes the inter term of its
-//     columns for all 64 tokens, the P V term from the chunk's score tiles,
-//     stores the outputs, and updates its columns of the state, decaying and
-//     splitting V in registers;
-//   * aux wave a (4..7) stages a quarter of every unit of tiles two chunks
-//     ahead (unit u: Q and K of chunk u, V of chunk u - 1) and computes the
-//     score tiles of the next chunk (dealt as for the score waves above),
-//     writing P (hi + lo) to LDS.
-// Q and K sit in a 3-slot ring (written at chunk x - 2, scored at x - 1, used
-// at x); V and P are double-buffered; one barrier per chunk.
-constexpr int kWideWaves = 8;
-constexpr int kWideNT = 64 * kWideWaves;
-struct WideSmem {
-    // first, so that every score-tile offset fits the 16-bit offset field of
-    // the LDS reads and one address register serves all of them
-    uint64_t p[2][10][2][64];    // [chunk parity][score tile][hi, lo][lane]: 4 bf16 each
-    uint16_t q[3][C * 128];
-    uint16_t k[3][C * 128];
-    uint16_t v[2][C * 128];      // token-major, K-tile swizzle
-};
-__device__ __forceinline__ constexpr int tile_id(int jt, int it) { return it * (it + 1) / 2 + jt; }
-
-// Score tiles of one chunk for aux wave A, into P slot ps.
-template <int A, bool kF>
-__device__ __forceinline__ void wide_scores(WideSmem &sm, int qs, int ps, const float (&mdec)[12], int g, int l16,
-                                            int lane) {
-    using T = Tiles<A>;
-    constexpr int KS = 4;
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    u16x8 kf[2][KS], qf[2][KS];
-#pragma unroll
-    for (int a = 0; a < T::nj; ++a)
-#pragma unroll
-        for (int s = 0; s < KS; ++s) kf[a][s] = lds8(&sm.k[qs][k_off<128>(16 * T::jl[a] + l16, 32 * s + 8 * g)]);
-#pragma unroll
-    for (int b = 0; b < T::ni; ++b)
-#pragma unroll
-        for (int s = 0; s < KS; ++s) qf[b][s] = lds8(&sm.q[qs][q_off<128>(16 * T::il[b] + l16, 32 * s + 8 * g)]);
-    f32x4 sc[3];
-#pragma unroll
-    for (int t = 0; t < T::n; ++t) sc[t] = z;
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-#pragma unroll
-        for (int t = 0; t < T::n; ++t) sc[t] = mma(kf[T::tj[t]][s], qf[T::ti[t]][s], sc[t]);
-#pragma unroll
-    for (int t = 0; t < T::n; ++t) {
-        f32x4 x;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) x[r] = sc[t][r] * mdec[4 * t + r];
-        u16x4 hi, lo;
-        split4(x, hi, lo);
-        const int id = tile_id(T::jl[T::tj[t]], T::il[T::ti[t]]);
-        sm.p[ps][id][0][lane] = __builtin_bit_cast(uint64_t, hi);
-        sm.p[ps][id][1][lane] = __builtin_bit_cast(uint64_t, lo);
-    }
-}
-
-template <int W, bool kF>
-__device__ __forceinline__ void wide_wave(WideSmem &sm, const Job &jb) {
-    constexpr bool kState = W < 4;
-    constexpr int R = W & 3;
-    const int lane = threadIdx.x & 63;
-    const int l16 = lane & 15, g = lane >> 4;
-    const float lam = jb.lam;
-    const float scale = kScale<128>;
-    const int64_t len = jb.len;
-    const int n = static_cast<int>((len + C - 1) / C);
-    const int c_last = static_cast<int>(len - static_cast<int64_t>(n - 1) * C);
-    const float sigma = kF ? expf(-32.f * lam) : 1.f;
-    const float vshift = kF ? 32.f : 0.f;
-    const uint32_t row = static_cast<uint32_t>(jb.row);
-    const uint32_t kvrow = static_cast<uint32_t>(jb.kvrow);
-    auto chunk_t = [&](int c) { return jb.t0 + static_cast<int64_t>(c) * C; };
-    auto chunk_c = [&](int c) { return c + 1 == n ? c_last : C; };
-
-    // ---- state wave: columns 32R .. 32R + 31, tile mt row r is state row 16 mt + 4g + r
-    f32x4 S[8][2];
-    float qdec[4], fin[4], er[4];
-    if constexpr (kState) {
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int nn = 0; nn < 2; ++nn)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    S[mt][nn][r] = sigma * jb.state_in[(16 * mt + 4 * g + r) * 128 + 32 * R + 16 * nn + l16];
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            qdec[it] = expf(-lam * static_cast<float>(16 * it + l16 + 1));
-            fin[it] = kF ? scale * expf(-lam * static_cast<float>(16 * it + l16 - 31)) : scale;
-            er[it] = expf(lam * static_cast<float>(it));
-        }
-    }
-    const float dc_full = expf(-lam * static_cast<float>(C));
-    const float dc_last = expf(-lam * static_cast<float>(c_last));
-    // byte offsets of the lane's transposed reads in a K or V tile: rows 4g +
-    // (l16 >> 2) (+ 16 h + 32 s2, which leaves the swizzle unchanged and is
-    // added as an immediate), columns 16 m + 4 (l16 & 3)
-    uint32_t ktr[8], vtr[2];
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) ktr[mt] = 2u * k_off<128>(4 * g + (l16 >> 2), 16 * mt + 4 * (l16 & 3));
-#pragma unroll
-    for (int nn = 0; nn < 2; ++nn) vtr[nn] = 2u * k_off<128>(4 * g + (l16 >> 2), 32 * R + 16 * nn + 4 * (l16 & 3));
-
-    auto state_step = [&](int ci) {
-        const bool last = ci + 1 == n;
-        const int c = last ? c_last : C;
-        const uint16_t *sq = sm.q[ci % 3];
-        const uint16_t *sk = sm.k[ci % 3];
-        const uint16_t *sv = sm.v[ci & 1];
-        const int ps = ci & 1;
-        // raw V^T of the wave's columns: [n][s2] holds tokens 32 s2 + 16 h + 4g + r
-        const uint32_t vbase = lds_addr(sv);
-        u16x8 vr[2][2];
-#pragma unroll
-        for (int nn = 0; nn < 2; ++nn) {
-            vr[nn][0] = cat(tr_off<0>(vbase + vtr[nn]), tr_off<16 * 256>(vbase + vtr[nn]));
-            vr[nn][1] = cat(tr_off<32 * 256>(vbase + vtr[nn]), tr_off<48 * 256>(vbase + vtr[nn]));
-        }
-        // inter term O^T[col][i] = sum_k S^T[col][k] Q^T[k][i]
-        f32x4 O[2][4];
-#pragma unroll
-        for (int nn = 0; nn < 2; ++nn)
-#pragma unroll
-            for (int it = 0; it < 4; ++it) O[nn][it] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            u16x8 sh[2], sl[2];
-#pragma unroll
-            for (int nn = 0; nn < 2; ++nn) {
-                u16x4 h0, l0, h1, l1;
-                split4(S[2 * ks][nn], h0, l0);
-                split4(S[2 * ks + 1][nn], h1, l1);
-                sh[nn] = cat(h0, h1);
-                sl[nn] = cat(l0, l1);
-            }
-#pragma unroll
-            for (int it = 0; it < 4; ++it) {
-                const int qr = 16 * it + l16;
-                const u16x8 qb = cat(lds4_single(&sq[q_off<128>(qr, 32 * ks + 4 * g)]),
-                                     lds4_single(&sq[q_off<128>(qr, 32 * ks + 16 + 4 * g)]));
-#pragma unroll
-                for (int nn = 0; nn < 2; ++nn) {
-                    O[nn][it] = mma(sh[nn], qb, O[nn][it]);
-                    O[nn][it] = mma(sl[nn], qb, O[nn][it]);
-                }
-            }
-        }
-        if constexpr (!kF) {
-#pragma unroll
-            for (int nn = 0; nn < 2; ++nn)
-#pragma unroll
-                for (int it = 0; it < 4; ++it) O[nn][it] *= qdec[it];
-        }
-        lds_wait();
-#pragma unroll
-        for (int nn = 0; nn < 2; ++nn)
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) pin(vr[nn][s2]);
-        // intra term O^T[col][i] += sum_j V^T[col][j] P^T[j][i], j-tiles 2 s2, 2 s2 + 1 <= i-tile
-        const u16x4 z4 = {0, 0, 0, 0};
-#pragma unroll
-        for (int it = 0; it < 4; ++it)
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const int ta = 2 * s2, tb = 2 * s2 + 1;
-                if (ta > it) continue;
-                const u16x4 ah = __builtin_bit_cast(u16x4, sm.p[ps][tile_id(ta, it)][0][lane]);
-                const u16x4 al = __builtin_bit_cast(u16x4, sm.p[ps][tile_id(ta, it)][1][lane]);
-                const u16x4 bh4 = tb <= it ? __builtin_bit_cast(u16x4, sm.p[ps][tile_id(tb, it)][0][lane]) : z4;
-                const u16x4 bl4 = tb <= it ? __builtin_bit_cast(u16x4, sm.p[ps][tile_id(tb, it)][1][lane]) : z4;
-                const u16x8 bh = cat(ah, bh4), bl = cat(al, bl4);
-#pragma unroll
-                for (int nn = 0; nn < 2; ++nn) {
-                    O[nn][it] = mma(vr[nn][s2], bh, O[nn][it]);
-                    O[nn][it] = mma(vr[nn][s2], bl, O[nn][it]);
-                }
-            }
-        // outputs: O^T tile (nn, it) element r is column 32R + 16nn + 4g + r, token 16 it + l16
-        char *ob = reinterpret_cast<char *>(jb.out + chunk_t(ci) * jb.row + jb.hcol + 32 * R);
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            if (last && 16 * it + l16 >= c) continue;
-#pragma unroll
-            for (int nn = 0; nn < 2; ++nn) {
-                const f32x4 o = O[nn][it] * fin[it];
-                const uint32_t offo = 2u * (static_cast<uint32_t>(16 * it + l16) * row + 16 * nn + 4 * g);
-                *reinterpret_cast<uint64_t *>(ob + offo) =
-                    (uint64_t)cvt2(o[0], o[1]) | ((uint64_t)cvt2(o[2], o[3]) << 32);
-            }
-        }
-        // update S = e^{-l c} S + K^T Vd, Vd = decayed V of the wave's columns (hi + lo)
-        const float dc = last ? dc_last : dc_full;
-        const uint32_t kbase = lds_addr(sk);
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int nn = 0; nn < 2; ++nn) S[mt][nn] *= dc;
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            u16x8 ka[8];
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                const uint32_t a = kbase + ktr[mt];
-                ka[mt] = s2 == 0 ? cat(tr_off<0>(a), tr_off<16 * 256>(a)) : cat(tr_off<32 * 256>(a), tr_off<48 * 256>(a));
-            }
-            u16x8 vh[2], vl[2];
-#pragma unroll
-            for (int nn = 0; nn < 2; ++nn) {
-                u16x4 hh[2], ll[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int j0 = 32 * s2 + 16 * h + 4 * g;
-                    const float w0 = expf(-lam * (static_cast<float>(c - 1 - j0) + vshift));
-                    f32x4 x;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        x[r] = j0 + r < c ? bf16_to_f32(vr[nn][s2][4 * h + r]) * (w0 * er[r]) : 0.f;
-                    split4(x, hh[h], ll[h]);
-                }
-                vh[nn] = cat(hh[0], hh[1]);
-                vl[nn] = cat(ll[0], ll[1]);
-            }
-            lds_wait();
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt) pin(ka[mt]);
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-                for (int nn = 0; nn < 2; ++nn) {
-                    S[mt][nn] = mma(ka[mt], vh[nn], S[mt][nn]);
-                    S[mt][nn] = mma(ka[mt], vl[nn], S[mt][nn]);
-                }
-        }
-    };
-
-    // ---- aux wave: staging of 4 of the 16 1-KB blocks of each of Q, K, V, and scores
-    float mdec[12];
-    if constexpr (!kState) score_weights<R, kF>(lam, g, l16, n == 1 ? c_last : C, mdec);
-    int qrow[4], qunit[4], kunit[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        qrow[b] = 4 * (4 * R + b) + lane / 16;
-        qunit[b] = (lane % 16) ^ swz_q<128>(qrow[b]);
-        kunit[b] = (lane % 16) ^ swz_k<128>(qrow[b]);
-    }
-    u16x8 rq[2][4], rk[2][4], rv[2][4];
-    auto load = [&](int u, int set) {  // unit u: Q, K of chunk u and V of chunk u - 1 (clamped)
-        const int cq = u < n ? u : n - 1;
-        const int cv = u - 1 < 0 ? 0 : (u - 1 < n ? u - 1 : n - 1);
-        const int lq = chunk_c(cq), lv = chunk_c(cv);
-        const uint16_t *qb = jb.q + chunk_t(cq) * jb.row + jb.hcol;
-        const uint16_t *kb = jb.k + chunk_t(cq) * jb.kvrow + jb.kvcol;
-        const uint16_t *vb = jb.v + chunk_t(cv) * jb.kvrow + jb.kvcol;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const uint32_t rq_ = static_cast<uint32_t>(qrow[b] < lq ? qrow[b] : lq - 1);
-            const uint32_t rv_ = static_cast<uint32_t>(qrow[b] < lv ? qrow[b] : lv - 1);
-            rq[set][b] = *reinterpret_cast<const u16x8 *>(qb + (rq_ * row + 8 * qunit[b]));
-            rk[set][b] = *reinterpret_cast<const u16x8 *>(kb + (rq_ * kvrow + 8 * kunit[b]));
-            rv[set][b] = *reinterpret_cast<const u16x8 *>(vb + (rv_ * kvrow + 8 * kunit[b]));
-        }
-    };
-    auto store = [&](int u, int set) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int dst = 512 * (4 * R + b) + 8 * lane;
-            if (u < n) {
-                *reinterpret_cast<u16x8 *>(&sm.q[u % 3][dst]) = rq[set][b];
-                *reinterpret_cast<u16x8 *>(&sm.k[u % 3][dst]) = rk[set][b];
-            }
-            if (u >= 1 && u - 1 < n) *reinterpret_cast<u16x8 *>(&sm.v[(u - 1) & 1][dst]) = rv[set][b];
-        }
-    };
-    auto scores = [&](int x) {  // chunk x
-        if (x + 1 == n && c_last != C && n > 1) score_weights<R, kF>(lam, g, l16, c_last, mdec);
-        wide_scores<R, kF>(sm, x % 3, x & 1, mdec, g, l16, lane);
-    };
-
-    if constexpr (!kState) {
-        load(0, 0);
-        load(1, 1);
-        store(0, 0);
-        store(1, 1);
-        load(2, 0);
-        load(3, 1);
-    }
-    __syncthreads();
-    if constexpr (!kState) scores(0);
-    // chunk ci: aux waves write unit ci + 2 (register set ci % 2), load unit
-    // ci + 4 into it and score chunk ci + 1; state waves compute chunk ci
-    auto step = [&](int ci, int set) {
-        lds_barrier();
-        if constexpr (!kState) {
-            store(ci + 2, set);
-            load(ci + 4, set);
-            if (ci + 1 < n) scores(ci + 1);
-        } else {
-            state_step(ci);
-        }
-    };
-    int ci = 0;
-#pragma unroll 1
-    for (; ci + 1 < n; ci += 2) {
-        step(ci, 0);
-        step(ci + 1, 1);
-    }
-    if (ci < n) step(ci, 0);
-    if constexpr (!kState) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // drain the loads past the end
-    } else {
-        const float unscale = kF ? expf(32.f * lam) : 1.f;
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-            for (int nn = 0; nn < 2; ++nn)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    jb.state_out[(16 * mt + 4 * g + r) * 128 + 32 * R + 16 * nn + l16] = S[mt][nn][r] * unscale;
-    }
-}
-
-// Workgroup (segment seg, pair): pairs are dealt in order of decreasing request
-// length for batches of up to kSortMax requests (see request_of_rank).
-__global__ __launch_bounds__(kWideNT) void prefill_wide_kernel(PrefillArgs a) {
-    __shared__ WideSmem sm;
-    __shared__ int sort_lens[kSortMax];
-    __shared__ int sort_pick;
-    const int H = a.num_heads;
-    const int seg = static_cast<int>(blockIdx.x) / a.pairs;
-    const int pair = static_cast<int>(blockIdx.x) - seg * a.pairs;
-    const int batch = a.pairs / H;
-    int b = pair / H;
-    const int h = pair - b * H;
-    const int tid = threadIdx.x;
-    if (batch > 1 && batch <= kSortMax) b = request_of_rank(a, batch, b, sort_lens, &sort_pick);
-    int64_t t0, t1;
-    request_range(a, b, t0, t1);
-    int64_t len = t1 - t0;
-    int nseg = 1;
-    if (a.segments > 1) {
-        const SegGeom sg = seg_geom(len, a.segments);
-        if (seg >= sg.ne) return;
-        const int64_t s0 = static_cast<int64_t>(seg) * sg.cps * C;
-        t0 += s0;
-        len = len - s0 < static_cast<int64_t>(sg.cps) * C ? len - s0 : static_cast<int64_t>(sg.cps) * C;
-        nseg = sg.ne;
-    }
-    const size_t row = static_cast<size_t>(H) * 128;
-    const size_t hcol = static_cast<size_t>(h) * 128;
-    const int slot = a.slot_idx[b];
-    if (slot < 0 || slot >= a.pool_slots) {
-        for (int64_t idx = tid; idx < len * 16; idx += kWideNT) {
-            const int64_t t = t0 + idx / 16;
-            *reinterpret_cast<u16x8 *>(a.out + t * row + hcol + 8 * (idx % 16)) = u16x8{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-        return;
-    }
-    if (len <= 0) return;
-    float *state = a.pool + (static_cast<size_t>(slot) * H + h) * (128 * 128);
-    float *s_in = state, *s_out = state;
-    if (nseg > 1) {
-        s_in = seg_slice<128>(a, b * H + h, seg);
-        if (seg < nseg - 1) s_out = s_in;
-    }
-    const int hk = h / (H / a.num_kv_heads);
-    const Job jb{a.q, a.k, a.v, a.out, s_in, s_out, t0, len, row, hcol,
-                 static_cast<size_t>(a.num_kv_heads) * 128, static_cast<size_t>(hk) * 128, 0, a.slopes[h]};
-    const bool factored = jb.lam >= 0.f && jb.lam <= 2.f;
-    switch (__builtin_amdgcn_readfirstlane(tid >> 6) + (factored ? 0 : 8)) {
-    case 0: wide_wave<0, true>(sm, jb); break;
-    case 1: wide_wave<1, true>(sm, jb); break;
-    case 2: wide_wave<2, true>(sm, jb); break;
-    case 3: wide_wave<3, true>(sm, jb); break;
-    case 4: wide_wave<4, true>(sm, jb); break;
-    case 5: wide_wave<5, true>(sm, jb); break;
-    case 6: wide_wave<6, true>(sm, jb); break;
-    case 7: wide_wave<7, true>(sm, jb); break;
-    case 8: wide_wave<0, false>(sm, jb); break;
-    case 9: wide_wave<1, false>(sm, jb); break;
-    case 10: wide_wave<2, false>(sm, jb); break;
-    case 11: wide_wave<3, false>(sm, jb); break;
-    case 12: wide_wave<4, false>(sm, jb); break;
-    case 13: wide_wave<5, false>(sm, jb); break;
-    case 14: wide_wave<6, false>(sm, jb); break;
-    default: wide_wave<7, false>(sm, jb); break;
-    }
-}
-
 // Step 2: workgroup `unit` turns the pool state and the sub-segment
 // contributions of its column block into the initial states S_0 .. S_{ne-1}:
 // S_{s+1} is S_s carried through the sub-segments q of segment s,
@@ -1608,33 +1202,16 @@ int choose_segments(int units, int max_seqlen, bool track) {
     return ns < 1 ? 1 : ns;
 }
 
-// The full-width kernel (one workgroup per request, head and segment) serves
-// D = 128 launches without snapshots when LA_PREFILL_WIDE=1.
-bool use_wide(int head_dim, bool track) {
-    if (head_dim != 128 || track) return false;
-    const char *env = std::getenv("LA_PREFILL_WIDE");
-    return env && env[0] == '1';
-}
-
 template <int D> hipError_t launch(const PrefillArgs &a, int batch, int max_seqlen, hipStream_t stream) {
     PrefillArgs copy = a;
     copy.pairs = batch * a.num_heads;
     const unsigned units = static_cast<unsigned>(copy.pairs) * Geo<D>::NVB;
-    const bool wide = use_wide(D, a.track_lens != nullptr);
-    copy.segments = choose_segments(wide ? copy.pairs : static_cast<int>(units), max_seqlen,
-                                    a.track_lens != nullptr);
+    copy.segments = choose_segments(static_cast<int>(units), max_seqlen, a.track_lens != nullptr);
     copy.seg_ws = nullptr;
     void *args[] = {&copy};
-    // the last launch: all (request, head, segment) work
-    auto main_launch = [&]() {
-        if (wide)
-            return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_wide_kernel),
-                                   dim3(static_cast<unsigned>(copy.pairs) * copy.segments), dim3(kWideNT), args, 0,
-                                   stream);
-        return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_chunked_kernel<D>), dim3(units * copy.segments),
-                               dim3(NT), args, 0, stream);
-    };
-    if (copy.segments == 1) return main_launch();
+    if (copy.segments == 1)
+        return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_chunked_kernel<D>), dim3(units), dim3(NT),
+                               args, 0, stream);
     // sub-segments: enough state-only workgroups to fill the CUs
     const int per = copy.pairs * (copy.segments - 1);
     int sub = cu_count() / per;
@@ -1646,7 +1223,8 @@ template <int D> hipError_t launch(const PrefillArgs &a, int batch, int max_seql
         // no workspace (out of memory, no stream-ordered pool): run unsplit
         (void)hipGetLastError();
         copy.segments = 1;
-        return main_launch();
+        return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_chunked_kernel<D>), dim3(units), dim3(NT),
+                               args, 0, stream);
     }
     copy.seg_ws = static_cast<float *>(ws);
     e = hipLaunchKernel(reinterpret_cast<const void *>(&prefill_delta_full_kernel<D>),
@@ -1654,7 +1232,9 @@ template <int D> hipError_t launch(const PrefillArgs &a, int batch, int max_seql
     if (e == hipSuccess)
         e = hipLaunchKernel(reinterpret_cast<const void *>(&prefill_combine_kernel<D>), dim3(units),
                             dim3(kCombineThreads), args, 0, stream);
-    if (e == hipSuccess) e = main_launch();
+    if (e == hipSuccess)
+        e = hipLaunchKernel(reinterpret_cast<const void *>(&prefill_chunked_kernel<D>),
+                            dim3(units * copy.segments), dim3(NT), args, 0, stream);
     const hipError_t f = hipFreeAsync(ws, stream);
     return e != hipSuccess ? e : f;
 }
