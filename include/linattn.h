@@ -118,11 +118,14 @@ la_status la_alibi_slopes(int num_heads, int layer_id, int num_layers, float *sl
  * the GPU's compute units, the longest request has at least 8192 tokens and
  * there are no track arrays, every request is split into up to 8 sequence
  * segments of at least 1024 tokens of the longest request, run side by side
- * from initial states that a state-only pass and a combine step compute first (the env var LA_PREFILL_MAX_SEGMENTS caps the
- * count; 1 turns the split off).  That path allocates a stream-ordered
- * workspace of batch*H*segments*d*d floats with hipMallocAsync on `stream` and
- * frees it with hipFreeAsync after the last launch (if that allocation fails
- * the call runs unsplit); results agree with the unsplit call to rounding.
+ * from initial states that a state-only pass and a combine step compute
+ * first (the env var LA_PREFILL_MAX_SEGMENTS caps the count; 1 turns the
+ * split off).  That path allocates a stream-ordered
+ * workspace of batch*H*(segments + (segments-1)*subsegs)*d*d floats (subsegs
+ * = 1..4 state-only workgroups per segment, as many as fill the compute
+ * units) with hipMallocAsync on `stream` and frees it with hipFreeAsync after
+ * the last launch (if that allocation fails the call runs unsplit); results
+ * agree with the unsplit call to rounding.
  * fp32: token-recurrent fp32 kernel.
  * Errors: LA_ERR_INVALID_ARG for NULL or misaligned pointers (q/k/v/out may be
  * NULL only when total_tokens == 0), negative sizes, num_kv_heads not dividing num_heads,
