@@ -129,6 +129,19 @@ def _qkv_shapes(q, k, v, out, what):
     return N, H, k.shape[1], d
 
 
+def _pool_and_slopes(state_pool, slopes, H, d, *others):
+    """The kernels index the pool as [P, H, d, d] and read H slopes: a tensor
+    of another shape would send them past its allocation, so check here (the C
+    ABI sees only pointers).  Every tensor must sit on the pool's device."""
+    if state_pool.dim() != 4 or _shape(state_pool)[1:] != (H, d, d):
+        raise ValueError(f"state_pool must be [P, H, d, d] = [P, {H}, {d}, {d}], got {_shape(state_pool)}")
+    if slopes.numel() != H:
+        raise ValueError(f"slopes must have one entry per head ({H}), got {slopes.numel()}")
+    for t in (slopes,) + others:
+        if t is not None and t.numel() and t.device != state_pool.device:
+            raise ValueError(f"all tensors must be on {state_pool.device}, found one on {t.device}")
+
+
 def la_prefill(q, k, v, cu_seqlens, state_pool, slot_idx, slopes, out, max_seqlen,
                track_lens=None, track_slot_idx=None, stream=None):
     """Packed varlen prefill.  q, out: [T, H, d]; k, v: [T, Hkv, d] (bf16 or fp32,
@@ -148,6 +161,7 @@ def la_prefill(q, k, v, cu_seqlens, state_pool, slot_idx, slopes, out, max_seqle
         raise ValueError("track_lens and track_slot_idx go together")
     if track_lens is not None and (track_lens.numel() != B or track_slot_idx.numel() != B):
         raise ValueError("track arrays must have one entry per request")
+    _pool_and_slopes(state_pool, slopes, H, d, q, k, v, out, cu_seqlens, slot_idx, track_lens, track_slot_idx)
     i32 = (torch.int32,)
     rc = load().la_prefill(_ptr(q, "q", io), _ptr(k, "k", io), _ptr(v, "v", io), _io_dtype(q),
                            _ptr(cu_seqlens, "cu_seqlens", i32), B, T, int(max_seqlen), H, HK, d,
@@ -169,6 +183,7 @@ def la_decode(q, k, v, state_pool, slot_idx, slopes, out, stream=None):
     B, H, HK, d = _qkv_shapes(q, k, v, out, "B")
     if slot_idx.numel() != B:
         raise ValueError("slot_idx must have one entry per request")
+    _pool_and_slopes(state_pool, slopes, H, d, q, k, v, out, slot_idx)
     rc = load().la_decode(_ptr(q, "q", io), _ptr(k, "k", io), _ptr(v, "v", io), _io_dtype(q), B, H,
                           HK, d, _ptr(state_pool, "state_pool", (torch.float32,)),
                           state_pool.shape[0], _ptr(slot_idx, "slot_idx", (torch.int32,), True),
@@ -190,6 +205,7 @@ def la_verify(q, k, v, num_draft, state_pool, slot_idx, slopes, out, state_out=N
         raise ValueError("q must hold num_draft tokens per request")
     if state_out is not None and _shape(state_out) != (B, H, d, d):
         raise ValueError("state_out must be [B, H, d, d]")
+    _pool_and_slopes(state_pool, slopes, H, d, q, k, v, out, slot_idx, state_out)
     rc = load().la_verify(_ptr(q, "q", io), _ptr(k, "k", io), _ptr(v, "v", io), _io_dtype(q), B,
                           int(num_draft), H, HK, d, _ptr(state_pool, "state_pool", (torch.float32,)),
                           state_pool.shape[0], _ptr(slot_idx, "slot_idx", (torch.int32,), True),
@@ -216,6 +232,7 @@ def la_verify_tree(q, k, v, num_draft, state_pool, slot_idx, parent_idx, slopes,
         raise ValueError("parent_idx must be [B, num_draft]")
     if draft_states is not None and _shape(draft_states) != (B, n, H, d, d):
         raise ValueError("draft_states must be [B, num_draft, H, d, d]")
+    _pool_and_slopes(state_pool, slopes, H, d, q, k, v, out, slot_idx, parent_idx, draft_states)
     rc = load().la_verify_tree(_ptr(q, "q", io), _ptr(k, "k", io), _ptr(v, "v", io), _io_dtype(q),
                                B, n, H, HK, d, _ptr(state_pool, "state_pool", (torch.float32,)),
                                state_pool.shape[0], _ptr(slot_idx, "slot_idx", (torch.int32,), True),

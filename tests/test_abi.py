@@ -180,3 +180,24 @@ def test_binding_rejects_host_tensors(lib):
         la.la_decode(q, q, q, pool, torch.zeros(3, dtype=torch.int32), torch.zeros(2), q)
     with pytest.raises(TypeError):
         la.la_decode(q, q, q.float(), pool, torch.zeros(3, dtype=torch.int32), torch.zeros(2), q)
+
+
+def test_binding_rejects_pool_and_slopes_of_the_wrong_shape(lib):
+    """The kernels index the pool as [P, H, d, d] and read H slopes; the
+    binding refuses other shapes before any HIP call."""
+    q = torch.zeros(3, 2, 128, dtype=torch.bfloat16)
+    slot = torch.zeros(3, dtype=torch.int32)
+    good_pool, good_slopes = torch.zeros(4, 2, 128, 128), torch.zeros(2)
+    cu = torch.tensor([0, 1, 2, 3], dtype=torch.int32)
+    for pool in (torch.zeros(4, 1, 128, 128), torch.zeros(4, 2, 64, 128), torch.zeros(4, 2 * 128 * 128)):
+        with pytest.raises(ValueError, match="state_pool"):
+            la.la_decode(q, q, q, pool, slot, good_slopes, q)
+        with pytest.raises(ValueError, match="state_pool"):
+            la.la_prefill(q, q, q, cu, pool, slot, good_slopes, q, 1)
+        with pytest.raises(ValueError, match="state_pool"):
+            la.la_verify(q, q, q, 1, pool, slot, good_slopes, q)
+    with pytest.raises(ValueError, match="slopes"):
+        la.la_decode(q, q, q, good_pool, slot, torch.zeros(3), q)
+    with pytest.raises(ValueError, match="slopes"):
+        la.la_verify_tree(q, q, q, 1, good_pool, slot, torch.full((3, 1), -1, dtype=torch.int32), torch.zeros(1),
+                          q)
