@@ -1112,18 +1112,22 @@ template <int D> __global__ __launch_bounds__(64 * kDeltaWaves) void prefill_del
     }
 }
 
-// Step 2: workgroup `unit` turns the pool state and the sub-segment
-// contributions of its column block into the initial states S_0 .. S_{ne-1}:
-// S_{s+1} is S_s carried through the sub-segments q of segment s,
-// S <- e^{-l n_q C} S + dS_{s,q}.  Each thread owns 4 consecutive columns of
-// some rows and loads every dS it needs before it runs the chain.
+// Step 2: the kCombineParts workgroups of a column block turn the pool state
+// and the sub-segment contributions of a quarter of its rows each into the
+// initial states S_0 .. S_{ne-1}: S_{s+1} is S_s carried through the
+// sub-segments q of segment s, S <- e^{-l n_q C} S + dS_{s,q}.  Each thread
+// owns 4 consecutive columns of some rows and loads every dS it needs before
+// it runs the chain.  (Workgroup x = part * units + unit.)
 constexpr int kCombineThreads = 256;
+constexpr int kCombineParts = 4;
 constexpr int kMaxSubsegs = 4;
 template <int D> __global__ __launch_bounds__(kCombineThreads) void prefill_combine_kernel(PrefillArgs a) {
     using G = Geo<D>;
     const int H = a.num_heads;
+    const int units = a.pairs * G::NVB;
+    const int part = static_cast<int>(blockIdx.x) / units;
     int pair, vb;
-    map_block<G::NVB>(static_cast<int>(blockIdx.x), a.pairs, pair, vb);
+    map_block<G::NVB>(static_cast<int>(blockIdx.x) - part * units, a.pairs, pair, vb);
     const int b = pair / H;
     const int h = pair - b * H;
     int64_t t0, t1;
@@ -1143,7 +1147,9 @@ template <int D> __global__ __launch_bounds__(kCombineThreads) void prefill_comb
         dq[q] = expf(-lam * static_cast<float>(n * C));
     }
     constexpr int kQuads = D * VB / 4;  // 4-column groups of the block
-    for (int e = threadIdx.x; e < kQuads; e += kCombineThreads) {
+    static_assert(kQuads % kCombineParts == 0, "rows split evenly");
+    constexpr int kPartQuads = kQuads / kCombineParts;
+    for (int e = part * kPartQuads + threadIdx.x; e < (part + 1) * kPartQuads; e += kCombineThreads) {
         const int idx = (e / (VB / 4)) * D + vb * VB + 4 * (e % (VB / 4));
         f32x4 ds[kMaxSegments - 1][kMaxSubsegs];
 #pragma unroll
@@ -1230,8 +1236,8 @@ template <int D> hipError_t launch(const PrefillArgs &a, int batch, int max_seql
     e = hipLaunchKernel(reinterpret_cast<const void *>(&prefill_delta_full_kernel<D>),
                         dim3(static_cast<unsigned>(per * copy.subsegs)), dim3(64 * kDeltaWaves), args, 0, stream);
     if (e == hipSuccess)
-        e = hipLaunchKernel(reinterpret_cast<const void *>(&prefill_combine_kernel<D>), dim3(units),
-                            dim3(kCombineThreads), args, 0, stream);
+        e = hipLaunchKernel(reinterpret_cast<const void *>(&prefill_combine_kernel<D>),
+                            dim3(units * kCombineParts), dim3(kCombineThreads), args, 0, stream);
     if (e == hipSuccess)
         e = hipLaunchKernel(reinterpret_cast<const void *>(&prefill_chunked_kernel<D>),
                             dim3(units * copy.segments), dim3(NT), args, 0, stream);
