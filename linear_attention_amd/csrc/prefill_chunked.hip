@@ -274,10 +274,11 @@ template <> struct Tiles<3> {
 // restricted to its state rows R0..R0+HR-1 (R0 = RH HR) and column tile CH,
 // part[it], and the update of those rows, S[k][v] = e^{-l c} S + sum_j K[j][k]
 // Vd[j][v].  qdec[it]: weight of the inter term for token i = 16 it + l16
-// (only without kF); dc: e^{-l c}.
+// (only without kF); dcm1: e^{-l c} - 1 (the decay is applied as S + dcm1 S, which
+// keeps the decay rate exact to float rounding of dcm1 even for tiny l).
 template <int D, int RH, int CH, bool kF>
 __device__ __forceinline__ void state_chunk(const uint16_t *sq, const uint16_t *sk, const uint16_t *svh,
-                                            const uint16_t *svl, const float (&qdec)[4], float dc, int g,
+                                            const uint16_t *svl, const float (&qdec)[4], float dcm1, int g,
                                             int l16, f32x4 (&S)[Geo<D>::HMT], f32x4 (&part)[4]) {
     using G = Geo<D>;
     constexpr int R0 = RH * G::HR;
@@ -334,7 +335,7 @@ __device__ __forceinline__ void state_chunk(const uint16_t *sq, const uint16_t *
         vl[s2] = cat(ldtr_v(svl, 32 * s2, 16 * CH, g, l16), ldtr_v(svl, 32 * s2 + 16, 16 * CH, g, l16));
     }
 #pragma unroll
-    for (int mt = 0; mt < G::HMT; ++mt) S[mt] *= dc;
+    for (int mt = 0; mt < G::HMT; ++mt) S[mt] += dcm1 * S[mt];
     __builtin_amdgcn_sched_barrier(0);
     lds_wait();
 #pragma unroll
@@ -507,8 +508,8 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
     float qdec[4];
     float fin[2];
     f32x4 keep[2];  // the wave's own inter partials of those row blocks, until stored
-    const float dc_full = expf(-lam * static_cast<float>(C));
-    const float dc_last = expf(-lam * static_cast<float>(c_last));
+    const float dc_full = expm1f(-lam * static_cast<float>(C));  // e^{-l c} - 1
+    const float dc_last = expm1f(-lam * static_cast<float>(c_last));
     if constexpr (kState) {
 #pragma unroll
         for (int mt = 0; mt < G::HMT; ++mt)
@@ -960,12 +961,12 @@ __device__ __forceinline__ void delta_wave(DeltaSmem<D> &sm, const uint16_t *kb,
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int n = 0; n < NTW; ++n) acc[mt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const float dc = expf(-lam * static_cast<float>(C));
+    const float dcm1 = expm1f(-lam * static_cast<float>(C));  // e^{-l C} - 1
     auto update = [&](int buf) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int n = 0; n < NTW; ++n) acc[mt][n] *= dc;
+            for (int n = 0; n < NTW; ++n) acc[mt][n] += dcm1 * acc[mt][n];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
             u16x8 ka[MT], bh[NTW], bl[NTW];
@@ -1137,14 +1138,14 @@ template <int D> __global__ __launch_bounds__(kCombineThreads) void prefill_comb
     if (slot < 0 || slot >= a.pool_slots || sg.ne == 0) return;
     const float *state = a.pool + (static_cast<size_t>(slot) * H + h) * (D * D);
     const float lam = a.slopes[h];
-    float dq[kMaxSubsegs];  // decay over each sub-segment (0: empty)
+    float dq[kMaxSubsegs];  // decay over each sub-segment minus 1 (0: empty)
     int nq[kMaxSubsegs];
 #pragma unroll
     for (int q = 0; q < kMaxSubsegs; ++q) {
         int c0 = 0, n = 0;
         if (q < a.subsegs) subseg_range(sg.cps, a.subsegs, q, c0, n);
         nq[q] = n;
-        dq[q] = expf(-lam * static_cast<float>(n * C));
+        dq[q] = expm1f(-lam * static_cast<float>(n * C));
     }
     constexpr int kQuads = D * VB / 4;  // 4-column groups of the block
     static_assert(kQuads % kCombineParts == 0, "rows split evenly");
@@ -1166,7 +1167,7 @@ template <int D> __global__ __launch_bounds__(kCombineThreads) void prefill_comb
                 if (s + 1 < sg.ne) {
 #pragma unroll
                     for (int q = 0; q < kMaxSubsegs; ++q)
-                        if (nq[q] > 0) cur = dq[q] * cur + ds[s][q];
+                        if (nq[q] > 0) cur += dq[q] * cur + ds[s][q];
                 }
             }
         }

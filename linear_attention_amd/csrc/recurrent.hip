@@ -13,6 +13,8 @@
 // and moves it with coalesced 128-bit loads and stores (nontemporal: the state
 // is touched once per call).  The q.S column sums are reduced across the row
 // groups of a wave with cross-lane shuffles and across the 4 waves in LDS.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -122,6 +124,14 @@ __device__ __forceinline__ void zero_rows(T *out, int64_t t0, int64_t t1, size_t
             store4(out + t * row + static_cast<size_t>(h) * D + 4 * tid, f32x4{0, 0, 0, 0});
 }
 
+// x <- dhi x + t, one rounding, written in place: as plain code the compiler
+// emits the accumulate form, whose result lands in t's register, and the
+// loop-carried state then costs a copy and extra registers every step.
+__device__ __forceinline__ void decay_step(f32x4 &x, float dhi, f32x4 t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm("v_fma_f32 %0, %1, %0, %2" : "+v"(x[i]) : "v"(dhi), "v"(t[i]));
+}
+
 // kTrack: the prefill variant that may take a state-tracking snapshot
 template <typename T, int D, bool kTrack>
 __global__ __launch_bounds__(kThreads) void recurrent_kernel(RecurrentArgs a) {
@@ -172,8 +182,21 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(RecurrentArgs a) {
 
     f32x4 S[RPT];
     load_state<D>(s_in, soff, S);
-
-    const float decay = expf(-a.slopes[h]);
+    // fp32 inputs carry the decay e^{-l} as an unevaluated float pair
+    // dhi + dlo, every step rounded once: S <- round(dhi S + (dlo S + k v)).
+    // A single float factor misstates the decay rate by up to 2^-25 / l
+    // relative, and rounding S + (e^{-l} - 1) S on its own loses or doubles a
+    // decay below half an ulp of S every step; both compound over a request's
+    // tokens and over successive calls, which the fp32 bound of 1e-4 does not
+    // absorb for small slopes and long requests.  dlo comes from expm1f:
+    // e^{-l} - dhi = (1 - dhi) + expm1(-l), where 1 - dhi is exact.  bf16
+    // inputs keep the single factor (rate error below 1.2e-4 relative for
+    // l >= 2^-12): the pair's extra multiply per element and token costs
+    // chain verify ~13%.
+    constexpr bool kPair = std::is_same<T, float>::value;
+    const float lam = a.slopes[h];
+    const float dhi = expf(-lam);
+    const float dlo = kPair && dhi >= 0.5f ? (1.f - dhi) + expm1f(-lam) : 0.f;
 
     __shared__ f32x4 red[2][4][L::CG];
     int parity = 0;
@@ -188,7 +211,10 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(RecurrentArgs a) {
         f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
-            S[r] = decay * S[r] + kk[r] * vv;
+            if constexpr (kPair)
+                decay_step(S[r], dhi, dlo * S[r] + kk[r] * vv);
+            else
+                S[r] = dhi * S[r] + kk[r] * vv;
             o += qq[r] * S[r];
         }
         reduce_store<D>(o, red, parity, out + off);
@@ -240,7 +266,11 @@ __global__ __launch_bounds__(kThreads) void tree_kernel(TreeArgs a) {
     const int soff = (RPT * rg) * D + 4 * cg;
     const float *R = a.pool + (static_cast<size_t>(slot) * H + h) * sdd + soff;
     f32x4 A[RPT];
-    const float decay = expf(-a.slopes[h]);
+    // decay as in recurrent_kernel: a float pair for fp32 inputs
+    constexpr bool kPair = std::is_same<T, float>::value;
+    const float lam = a.slopes[h];
+    const float dhi = expf(-lam);
+    const float dlo = kPair && dhi >= 0.5f ? (1.f - dhi) + expm1f(-lam) : 0.f;
 
     auto kv = [&](int j, float (&kk)[RPT], f32x4 &vv) {
         const size_t kvoff = (t0 + j) * kvrow + static_cast<size_t>(hk) * D;
@@ -259,22 +289,31 @@ __global__ __launch_bounds__(kThreads) void tree_kernel(TreeArgs a) {
         const int p = par[j];
         if (p >= 0 && p == j - 1) {
 #pragma unroll
-            for (int r = 0; r < RPT; ++r) A[r] = decay * A[r] + kk[r] * vv;
+            for (int r = 0; r < RPT; ++r) {
+                if constexpr (kPair)
+                    decay_step(A[r], dhi, dlo * A[r] + kk[r] * vv);
+                else
+                    A[r] = dhi * A[r] + kk[r] * vv;
+            }
         } else if (p < 0) {
 #pragma unroll
-            for (int r = 0; r < RPT; ++r)
-                A[r] = decay * *reinterpret_cast<const f32x4 *>(R + r * D) + kk[r] * vv;
+            for (int r = 0; r < RPT; ++r) {
+                const f32x4 root = *reinterpret_cast<const f32x4 *>(R + r * D);
+                A[r] = kPair ? dhi * root + (dlo * root + kk[r] * vv) : dhi * root + kk[r] * vv;
+            }
         } else {
 #pragma unroll
             for (int r = 0; r < RPT; ++r) A[r] = kk[r] * vv;
-            float w = decay;
+            // the weight of an ancestor m steps up is dhi^m (m <= num_draft, so
+            // the factor's rounding stays below m 2^-25)
+            float w = dhi;
             for (int x = p; x >= 0; x = par[x]) {
                 float ka[RPT];
                 f32x4 va;
                 kv(x, ka, va);
 #pragma unroll
                 for (int r = 0; r < RPT; ++r) A[r] += (w * ka[r]) * va;
-                w *= decay;
+                w *= dhi;
             }
 #pragma unroll
             for (int r = 0; r < RPT; ++r) A[r] += w * *reinterpret_cast<const f32x4 *>(R + r * D);
