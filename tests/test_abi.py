@@ -201,3 +201,15 @@ def test_binding_rejects_pool_and_slopes_of_the_wrong_shape(lib):
     with pytest.raises(ValueError, match="slopes"):
         la.la_verify_tree(q, q, q, 1, good_pool, slot, torch.full((3, 1), -1, dtype=torch.int32), torch.zeros(1),
                           q)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """The product path has no fallback: without liblinattn.so, loading the
+    library and calling an entry point both raise ImportError."""
+    monkeypatch.setattr(la, "_lib", None)
+    monkeypatch.setattr(la, "LIB_PATH", str(tmp_path / "liblinattn.so"))
+    with pytest.raises(ImportError, match="not built"):
+        la.load()
+    q = torch.zeros(3, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ImportError, match="not built"):
+        la.la_decode(q, q, q, torch.zeros(4, 2, 128, 128), torch.zeros(3, dtype=torch.int32), torch.zeros(2), q)
