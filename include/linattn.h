@@ -42,10 +42,12 @@
  * every path).
  *
  * Calls are asynchronous on `stream` (0 = the null stream): the library does
- * no host synchronisation, no device-to-host reads and no allocation on these
- * paths (except the stream-ordered workspace of a prefill split into sequence
- * segments, see la_prefill), and keeps no state between calls.  The inputs must not alias out,
- * state_pool or state_out.  Overlapping calls that name the same pool slot race.
+ * no host synchronisation, no device-to-host reads and no allocation, and
+ * keeps no state between calls (beyond each device's compute-unit count,
+ * read once).  Scratch memory, where a call can use it, is the caller's:
+ * see la_prefill_workspace_bytes.  The inputs must not alias out, state_pool,
+ * state_out or the workspace.  Overlapping calls that name the same pool slot
+ * or share a workspace race.
  *
  * Errors: every call returns an la_status and never aborts.  Host-visible
  * arguments are validated before anything is launched.  Device-resident
@@ -97,6 +99,30 @@ const char *la_status_string(la_status s);
 la_status la_alibi_slopes(int num_heads, int layer_id, int num_layers, float *slopes_host);
 
 /*
+ * Workspace of a bf16 prefill, in bytes, on the current device: what
+ * la_prefill needs to split the requests of a call with these sizes into
+ * sequence segments (0 when such a call does not split).
+ *
+ * A bf16 launch whose (request, head, 32-column block) units fill only part of
+ * the GPU's compute units, whose longest request (max_seqlen) has at least
+ * 8192 tokens and which takes no snapshots splits every request into up to 8
+ * sequence segments of at least 1024 tokens of the longest request, as many
+ * as fill the compute units; the segments run side by side from initial
+ * states that a state-only pass and a combine step compute first.  The
+ * workspace holds their partial states: batch * num_heads * (segments +
+ * (segments - 1) * subsegs) * head_dim^2 floats, subsegs = 1..4 state-only
+ * workgroups per segment (as many as fill the compute units).  The size
+ * depends on the device's compute-unit count, so query it on the device the
+ * call will run on.  The environment variable LA_PREFILL_MAX_SEGMENTS (1..8)
+ * caps the segment count, in this query and in la_prefill alike.
+ * Invalid sizes (negative, head_dim other than 64/128) give 0.
+ * fp32 prefills and prefills with track arrays never split and need no
+ * workspace, whatever this returns.
+ */
+size_t la_prefill_workspace_bytes(int batch, int64_t total_tokens, int max_seqlen, int num_heads,
+                                  int head_dim);
+
+/*
  * Packed varlen prefill ("extend") over `batch` requests holding
  * `total_tokens` tokens in all ([LA-page] §独立参考实现 and
  * §输入与配置覆盖).  For every request the state is read from
@@ -114,32 +140,31 @@ la_status la_alibi_slopes(int num_heads, int layer_id, int num_layers, float *sl
  * Track slots must be distinct from each other and from every slot_idx entry.
  *
  * bf16 (d = 64 or 128): chunked MFMA kernel (fp32 state, bf16 hi/lo operand
- * splits).  When its (request, head, 32-column block) units fill only part of
- * the GPU's compute units, the longest request has at least 8192 tokens and
- * there are no track arrays, every request is split into up to 8 sequence
- * segments of at least 1024 tokens of the longest request, run side by side
- * from initial states that a state-only pass and a combine step compute
- * first (the env var LA_PREFILL_MAX_SEGMENTS caps the count; 1 turns the
- * split off).  That path allocates a stream-ordered
- * workspace of batch*H*(segments + (segments-1)*subsegs)*d*d floats (subsegs
- * = 1..4 state-only workgroups per segment, as many as fill the compute
- * units) with hipMallocAsync on `stream` and frees it with hipFreeAsync after
- * the last launch (if that allocation fails the call runs unsplit); results
- * agree with the unsplit call to rounding.
- * fp32: token-recurrent fp32 kernel.
+ * splits).  fp32: token-recurrent fp32 kernel.
+ *
+ * workspace, workspace_bytes: device scratch owned by the caller, 16-byte
+ * aligned, used only by a call that splits into sequence segments (see
+ * la_prefill_workspace_bytes for when and how much).  NULL with 0 bytes runs
+ * such a call unsplit (same results to rounding, slower on long requests); a
+ * non-NULL workspace smaller than the split needs is LA_ERR_INVALID_ARG.  Its
+ * contents before and after the call are of no meaning; the call reads only
+ * what it writes there first, in stream order.  The library never allocates.
+ *
  * Errors: LA_ERR_INVALID_ARG for NULL or misaligned pointers (q/k/v/out may be
- * NULL only when total_tokens == 0), negative sizes, num_kv_heads not dividing num_heads,
- * only one of the two track arrays, batch > pool_slots or, with LA_DEBUG=1,
- * inconsistent cu_seqlens/slot_idx/track arrays; LA_ERR_UNSUPPORTED for a
- * head_dim other than 64/128 or an unknown dtype; LA_ERR_HIP on a launch
- * failure.
+ * NULL only when total_tokens == 0), negative sizes, num_kv_heads not dividing
+ * num_heads, only one of the two track arrays, batch > pool_slots, a NULL
+ * workspace with nonzero workspace_bytes, a workspace too small for the
+ * split, or, with LA_DEBUG=1, inconsistent cu_seqlens/slot_idx/track arrays;
+ * LA_ERR_UNSUPPORTED for a head_dim other than 64/128 or an unknown dtype;
+ * LA_ERR_HIP on a launch failure.
  */
 la_status la_prefill(const void *q, const void *k, const void *v, la_dtype dtype,
                      const int32_t *cu_seqlens, int batch, int64_t total_tokens, int max_seqlen,
                      int num_heads, int num_kv_heads, int head_dim,
                      float *state_pool, int64_t pool_slots, const int32_t *slot_idx,
                      const int32_t *track_lens, const int32_t *track_slot_idx,
-                     const float *slopes, void *out, hipStream_t stream);
+                     const float *slopes, void *out, void *workspace, size_t workspace_bytes,
+                     hipStream_t stream);
 
 /*
  * Decode: one token per request (q, out are [batch, H, d]; k, v [batch, Hkv, d]).

@@ -24,8 +24,8 @@ LIB_PATH = os.path.join(_HERE, "liblinattn.so")
 LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, -1, -2, -3
 LA_DTYPE_BF16, LA_DTYPE_F32 = 0, 1
 
-EXPORTED = ("la_status_string", "la_alibi_slopes", "la_prefill", "la_decode", "la_verify",
-            "la_verify_tree")
+EXPORTED = ("la_status_string", "la_alibi_slopes", "la_prefill_workspace_bytes", "la_prefill",
+            "la_decode", "la_verify", "la_verify_tree")
 
 _lib = None
 
@@ -51,7 +51,9 @@ def load():
     lib.la_status_string.restype = ctypes.c_char_p
     lib.la_alibi_slopes.argtypes = [I, I, I, P]
     lib.la_alibi_slopes.restype = I
-    lib.la_prefill.argtypes = [P, P, P, I, P, I, L, I, I, I, I, P, L, P, P, P, P, P, P]
+    lib.la_prefill_workspace_bytes.argtypes = [I, L, I, I, I]
+    lib.la_prefill_workspace_bytes.restype = ctypes.c_size_t
+    lib.la_prefill.argtypes = [P, P, P, I, P, I, L, I, I, I, I, P, L, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.la_prefill.restype = I
     lib.la_decode.argtypes = [P, P, P, I, I, I, I, I, P, L, P, P, P, P]
     lib.la_decode.restype = I
@@ -142,14 +144,26 @@ def _pool_and_slopes(state_pool, slopes, H, d, *others):
             raise ValueError(f"all tensors must be on {state_pool.device}, found one on {t.device}")
 
 
+def la_prefill_workspace_bytes(batch: int, total_tokens: int, max_seqlen: int, num_heads: int,
+                               head_dim: int) -> int:
+    """Bytes of scratch a bf16 prefill of these sizes uses on the current device
+    (0 when it runs unsplit)."""
+    return int(load().la_prefill_workspace_bytes(int(batch), int(total_tokens), int(max_seqlen),
+                                                 int(num_heads), int(head_dim)))
+
+
 def la_prefill(q, k, v, cu_seqlens, state_pool, slot_idx, slopes, out, max_seqlen,
-               track_lens=None, track_slot_idx=None, stream=None):
+               track_lens=None, track_slot_idx=None, workspace="auto", stream=None):
     """Packed varlen prefill.  q, out: [T, H, d]; k, v: [T, Hkv, d] (bf16 or fp32,
     d = 64 or 128, Hkv dividing H); cu_seqlens [B+1] int32; state_pool
     [P, H, d, d] fp32 (updated in place); slot_idx [B] int32; slopes [H] fp32;
     max_seqlen: host int >= every length.  track_lens / track_slot_idx ([B] int32,
     both or neither): snapshot of request b's state after track_lens[b] tokens
-    written to pool slot track_slot_idx[b] (negative: none)."""
+    written to pool slot track_slot_idx[b] (negative: none).
+    workspace: a device tensor (any dtype, contiguous) lent to the call as
+    scratch; "auto" takes one of la_prefill_workspace_bytes(...) bytes from
+    torch's allocator on the pool's device; None runs a call that would split
+    into sequence segments unsplit."""
     import torch
 
     io = (torch.bfloat16, torch.float32)
@@ -162,6 +176,22 @@ def la_prefill(q, k, v, cu_seqlens, state_pool, slot_idx, slopes, out, max_seqle
     if track_lens is not None and (track_lens.numel() != B or track_slot_idx.numel() != B):
         raise ValueError("track arrays must have one entry per request")
     _pool_and_slopes(state_pool, slopes, H, d, q, k, v, out, cu_seqlens, slot_idx, track_lens, track_slot_idx)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError('workspace must be a tensor, None or "auto"')
+        need = 0
+        if q.dtype == torch.bfloat16 and track_lens is None:
+            with torch.cuda.device(state_pool.device):
+                need = la_prefill_workspace_bytes(B, T, max_seqlen, H, d)
+        workspace = torch.empty(need, dtype=torch.uint8, device=state_pool.device) if need else None
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or not workspace.is_contiguous():
+            raise TypeError("workspace must be a contiguous device tensor")
+        if workspace.device != state_pool.device:
+            raise ValueError(f"workspace must be on {state_pool.device}")
+        ws_bytes = workspace.numel() * workspace.element_size()
+        ws_ptr = workspace.data_ptr() if ws_bytes else None
     i32 = (torch.int32,)
     rc = load().la_prefill(_ptr(q, "q", io), _ptr(k, "k", io), _ptr(v, "v", io), _io_dtype(q),
                            _ptr(cu_seqlens, "cu_seqlens", i32), B, T, int(max_seqlen), H, HK, d,
@@ -170,7 +200,7 @@ def la_prefill(q, k, v, cu_seqlens, state_pool, slot_idx, slopes, out, max_seqle
                            _ptr(track_lens, "track_lens", i32, True),
                            _ptr(track_slot_idx, "track_slot_idx", i32, True),
                            _ptr(slopes, "slopes", (torch.float32,)), _ptr(out, "out", io),
-                           _stream(state_pool, stream))
+                           ws_ptr, ws_bytes, _stream(state_pool, stream))
     _check(rc, "la_prefill")
 
 

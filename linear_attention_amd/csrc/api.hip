@@ -5,18 +5,18 @@
 // 线性注意力测试覆盖深度解析" (www.2kiu.com/news/4599301) as [LA-page].
 #include <hip/hip_runtime.h>
 
-#include <cmath>
+#include <atomic>
 #include <cstdlib>
-#include <cstring>
 #include <vector>
 
-#include "common.h"
+#include "host_logic.h"
 #include "launch.h"
 #include "linattn.h"
 
-namespace {
+using la::aligned16;
+using la::common_checks;
 
-constexpr int64_t kMaxGrid = 0x7fffffff;
+namespace {
 
 bool debug_mode() {
     const char *s = std::getenv("LA_DEBUG");
@@ -29,10 +29,8 @@ bool copy_to_host(std::vector<T> &dst, const T *src, size_t n) {
     return n == 0 || hipMemcpy(dst.data(), src, sizeof(T) * n, hipMemcpyDeviceToHost) == hipSuccess;
 }
 
-// Debug-mode validation of device-resident metadata ([LA-page] §生产环境不支持
-// item 1: unsupported inputs are rejected before the kernel runs).  Synchronises
-// `stream`.  cu_seqlens may be null (fixed-length requests of `fixed_len`
-// tokens); track arrays and parents may be null.
+// Debug mode: copy the device metadata to the host (synchronising `stream`)
+// and check it there.
 la_status debug_check(const int32_t *cu_seqlens, int batch, int64_t total_tokens, int max_seqlen,
                       int fixed_len, const int32_t *slot_idx, int64_t pool_slots,
                       const int32_t *track_lens, const int32_t *track_slot_idx,
@@ -40,65 +38,38 @@ la_status debug_check(const int32_t *cu_seqlens, int batch, int64_t total_tokens
     std::vector<int32_t> slots, cu, tl, ts, par;
     if (hipStreamSynchronize(stream) != hipSuccess) return LA_ERR_HIP;
     if (!copy_to_host(slots, slot_idx, batch)) return LA_ERR_HIP;
-    std::vector<int64_t> lens(batch > 0 ? batch : 1, fixed_len);
-    if (cu_seqlens) {
-        if (!copy_to_host(cu, cu_seqlens, batch + 1)) return LA_ERR_HIP;
-        if (cu[0] != 0 || cu[batch] != total_tokens) return LA_ERR_INVALID_ARG;
-        for (int b = 0; b < batch; ++b) {
-            lens[b] = static_cast<int64_t>(cu[b + 1]) - cu[b];
-            if (lens[b] < 0 || lens[b] > max_seqlen) return LA_ERR_INVALID_ARG;
-        }
-    }
-    std::vector<char> seen(static_cast<size_t>(pool_slots), 0);
-    for (int b = 0; b < batch; ++b) {
-        const int32_t s = slots[b];
-        if (s < 0 || s >= pool_slots || seen[s]) return LA_ERR_INVALID_ARG;
-        seen[s] = 1;
-    }
-    if (track_lens) {
-        if (!copy_to_host(tl, track_lens, batch) || !copy_to_host(ts, track_slot_idx, batch))
-            return LA_ERR_HIP;
-        for (int b = 0; b < batch; ++b) {
-            if (ts[b] < 0) continue;  // no snapshot for this request
-            if (ts[b] >= pool_slots || seen[ts[b]] || tl[b] < 0 || tl[b] > lens[b])
-                return LA_ERR_INVALID_ARG;
-            seen[ts[b]] = 1;
-        }
-    }
-    if (parents) {
-        if (!copy_to_host(par, parents, static_cast<size_t>(batch) * fixed_len)) return LA_ERR_HIP;
-        for (size_t i = 0; i < static_cast<size_t>(batch) * fixed_len; ++i) {
-            const int j = static_cast<int>(i % fixed_len);
-            if (par[i] < -1 || par[i] >= j) return LA_ERR_INVALID_ARG;
-        }
-    }
-    return LA_OK;
-}
-
-// The kernels move q, k, v, out and states with 16-byte vector accesses.
-bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-la_status common_checks(const void *q, const void *k, const void *v, la_dtype dtype,
-                        int64_t total_tokens, int batch, int num_heads, int num_kv_heads,
-                        int head_dim, const float *state_pool, int64_t pool_slots,
-                        const int32_t *slot_idx, const float *slopes, const void *out) {
-    if (batch < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || pool_slots <= 0 ||
-        total_tokens < 0)
-        return LA_ERR_INVALID_ARG;
-    if (num_heads % num_kv_heads != 0) return LA_ERR_INVALID_ARG;
-    if (dtype != LA_DTYPE_BF16 && dtype != LA_DTYPE_F32) return LA_ERR_UNSUPPORTED;
-    if (head_dim != 128 && head_dim != 64) return LA_ERR_UNSUPPORTED;
-    if (batch > pool_slots) return LA_ERR_INVALID_ARG;  // slots must be distinct
-    if (!state_pool || !slopes || (batch > 0 && !slot_idx)) return LA_ERR_INVALID_ARG;
-    if (total_tokens > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(state_pool))
-        return LA_ERR_INVALID_ARG;
-    if (static_cast<int64_t>(batch) * num_heads * 4 > kMaxGrid) return LA_ERR_INVALID_ARG;
-    if (total_tokens > kMaxGrid) return LA_ERR_INVALID_ARG;  // int32 cu_seqlens
-    return LA_OK;
+    if (cu_seqlens && !copy_to_host(cu, cu_seqlens, batch + 1)) return LA_ERR_HIP;
+    if (track_lens && (!copy_to_host(tl, track_lens, batch) || !copy_to_host(ts, track_slot_idx, batch)))
+        return LA_ERR_HIP;
+    if (parents && !copy_to_host(par, parents, static_cast<size_t>(batch) * fixed_len)) return LA_ERR_HIP;
+    return la::check_metadata(cu_seqlens ? cu.data() : nullptr, batch, total_tokens, max_seqlen, fixed_len,
+                              slots.data(), pool_slots, track_lens ? tl.data() : nullptr,
+                              track_lens ? ts.data() : nullptr, parents ? par.data() : nullptr);
 }
 
 la_status from_hip(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_HIP; }
+
+// Compute units of the current device (cached per device).
+int cu_count() {
+    static std::atomic<int> count[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = count[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        count[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// The most sequence segments a prefill may use: kMaxSegments, lowered by the
+// environment variable LA_PREFILL_MAX_SEGMENTS (1 turns the split off).
+int segment_cap() {
+    int cap = la::kMaxSegments;
+    if (const char *env = std::getenv("LA_PREFILL_MAX_SEGMENTS")) cap = std::atoi(env);
+    return cap < 1 ? 1 : (cap > la::kMaxSegments ? la::kMaxSegments : cap);
+}
 
 }  // namespace
 
@@ -115,20 +86,14 @@ const char *la_status_string(la_status s) {
 }
 
 la_status la_alibi_slopes(int num_heads, int layer_id, int num_layers, float *slopes_host) {
-    if (num_heads <= 0 || num_layers <= 0 || layer_id < 0 || layer_id >= num_layers || !slopes_host)
-        return LA_ERR_INVALID_ARG;
-    int pow2 = 1;  // largest power of two <= num_heads
-    while (pow2 <= num_heads / 2) pow2 <<= 1;
-    const double layer = num_layers == 1
-                             ? 1.0 + 1e-5
-                             : 1.0 - static_cast<double>(layer_id) / static_cast<double>(num_layers - 1) + 1e-5;
-    for (int h = 0; h < num_heads; ++h) {
-        // geometric sequence 2^(-8(h+1)/pow2); the heads past pow2 take the odd
-        // positions of the 2*pow2 sequence, 2^(-4(2j+1)/pow2)
-        const double e = h < pow2 ? -8.0 * (h + 1) / pow2 : -4.0 * (2 * (h - pow2) + 1) / pow2;
-        slopes_host[h] = static_cast<float>(std::exp2(e) * layer);
-    }
-    return LA_OK;
+    return la::alibi_slopes(num_heads, layer_id, num_layers, slopes_host);
+}
+
+size_t la_prefill_workspace_bytes(int batch, int64_t total_tokens, int max_seqlen, int num_heads,
+                                  int head_dim) {
+    if (total_tokens < 0 || max_seqlen < 0) return 0;
+    return la::plan_segments(cu_count(), batch, num_heads, head_dim, max_seqlen, false, segment_cap())
+        .workspace_bytes;
 }
 
 la_status la_prefill(const void *q, const void *k, const void *v, la_dtype dtype,
@@ -136,12 +101,22 @@ la_status la_prefill(const void *q, const void *k, const void *v, la_dtype dtype
                      int num_heads, int num_kv_heads, int head_dim, float *state_pool,
                      int64_t pool_slots, const int32_t *slot_idx, const int32_t *track_lens,
                      const int32_t *track_slot_idx, const float *slopes, void *out,
-                     hipStream_t stream) {
+                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
     la_status st = common_checks(q, k, v, dtype, total_tokens, batch, num_heads, num_kv_heads,
                                  head_dim, state_pool, pool_slots, slot_idx, slopes, out);
     if (st != LA_OK) return st;
     if (max_seqlen < 0 || (batch > 0 && !cu_seqlens)) return LA_ERR_INVALID_ARG;
     if (!track_lens != !track_slot_idx) return LA_ERR_INVALID_ARG;
+    if ((!workspace && workspace_bytes != 0) || !aligned16(workspace)) return LA_ERR_INVALID_ARG;
+    la::SegmentPlan plan;
+    if (dtype == LA_DTYPE_BF16 && batch > 0 && !track_lens && max_seqlen >= la::kMinSplitTokens) {
+        plan = la::plan_segments(cu_count(), batch, num_heads, head_dim, max_seqlen, track_lens != nullptr,
+                                 segment_cap());
+        if (plan.segments > 1) {
+            if (!workspace) plan = la::SegmentPlan{};  // no workspace: run unsplit
+            else if (workspace_bytes < plan.workspace_bytes) return LA_ERR_INVALID_ARG;
+        }
+    }
     if (debug_mode()) {
         st = debug_check(cu_seqlens, batch, total_tokens, max_seqlen, 0, slot_idx, pool_slots,
                          track_lens, track_slot_idx, nullptr, stream);
@@ -166,7 +141,10 @@ la_status la_prefill(const void *q, const void *k, const void *v, la_dtype dtype
         a.track_slot_idx = track_slot_idx;
         a.slopes = slopes;
         a.out = static_cast<uint16_t *>(out);
-        return from_hip(la::launch_prefill_chunked(a, batch, head_dim, max_seqlen, stream));
+        a.segments = plan.segments;
+        a.subsegs = plan.subsegs;
+        a.seg_ws = plan.segments > 1 ? static_cast<float *>(workspace) : nullptr;
+        return from_hip(la::launch_prefill_chunked(a, batch, head_dim, stream));
     }
     la::RecurrentArgs a{};
     a.q = q;

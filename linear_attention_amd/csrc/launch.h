@@ -45,7 +45,9 @@ struct TreeArgs {
 hipError_t launch_tree(const TreeArgs &a, bool bf16, int head_dim, int batch, hipStream_t stream);
 
 // Chunked bf16 MFMA prefill (head_dim 128 or 64): one workgroup per (request,
-// head, 32-column block of the state), chunks of 64 tokens.
+// head, 32-column block of the state), chunks of 64 tokens.  With segments > 1
+// every request is split into that many sequence segments, using the caller's
+// workspace seg_ws (size and layout: plan_segments in host_logic.h).
 struct PrefillArgs {
     const uint16_t *q, *k, *v;
     const int32_t *cu_seqlens;
@@ -57,13 +59,10 @@ struct PrefillArgs {
     const int32_t *track_lens, *track_slot_idx;
     const float *slopes;
     uint16_t *out;
-    int segments;   // sequence segments per request (set by the launcher)
+    int segments;   // sequence segments per request (1: no split)
     int subsegs;    // sub-segments per segment in the state-only pass
-    float *seg_ws;  // their workspace (layout in prefill_chunked.hip)
+    float *seg_ws;  // their workspace (device memory, owned by the caller)
 };
-// max_seqlen: the longest request (decides how many segments a launch that
-// underfills the GPU splits requests into; any value gives the same results)
-hipError_t launch_prefill_chunked(const PrefillArgs &a, int batch, int head_dim, int max_seqlen,
-                                  hipStream_t stream);
+hipError_t launch_prefill_chunked(const PrefillArgs &a, int batch, int head_dim, hipStream_t stream);
 
 }  // namespace la

@@ -72,13 +72,14 @@
 #include <cstdlib>
 
 #include "common.h"
+#include "host_logic.h"
 #include "launch.h"
 
 namespace la {
 namespace {
 
-constexpr int C = 64;   // chunk length
-constexpr int VB = 32;  // state columns per workgroup
+constexpr int C = kChunk;      // chunk length
+constexpr int VB = kColBlock;  // state columns per workgroup
 
 // Geometry for head dimension D (128 or 64).  State wave (rh, ch) keeps the
 // state rows rh*HR .. rh*HR + HR - 1 of column tile ch (16 columns) of the
@@ -814,9 +815,8 @@ __device__ __forceinline__ int request_of_rank(const PrefillArgs &a, int batch, 
 //      recurrence at sub-segment granularity from the pool state S_0;
 //   3. prefill_chunked_kernel: every segment from its own initial state, as a
 //      request of its own; the last segment stores the final state.
-// All three use the workspace a.seg_ws in stream order; the pool slot is read
-// by step 2 only and written by step 3 only.
-constexpr int kMaxSegments = 8;  // sequence segments per request, at most
+// All three use the caller's workspace a.seg_ws in stream order; the pool slot
+// is read by step 2 only and written by step 3 only.
 struct SegGeom {
     int nchunks;  // chunks of the request
     int cps;      // chunks per segment
@@ -1121,7 +1121,6 @@ template <int D> __global__ __launch_bounds__(64 * kDeltaWaves) void prefill_del
 // it runs the chain.  (Workgroup x = part * units + unit.)
 constexpr int kCombineThreads = 256;
 constexpr int kCombineParts = 4;
-constexpr int kMaxSubsegs = 4;
 template <int D> __global__ __launch_bounds__(kCombineThreads) void prefill_combine_kernel(PrefillArgs a) {
     using G = Geo<D>;
     const int H = a.num_heads;
@@ -1174,85 +1173,38 @@ template <int D> __global__ __launch_bounds__(kCombineThreads) void prefill_comb
     }
 }
 
-// Segments for a launch of `units` (request, head, column block) units: as
-// many as fill the GPU's CUs, at most kMaxSegments (or LA_PREFILL_MAX_SEGMENTS
-// when set, 1 turning segments off), each at least kMinSegmentTokens of the
-// longest request.  A split call pays a fixed cost (the workspace, two more
-// launches, ~20-40 us when its kernels are short), so only launches whose
-// longest request has kMinSplitTokens or more are split: measured at 8 heads,
-// a 4096-token request gains nothing, 8192 tokens go from 152 to 93 us.
-// Snapshot requests are never split.
-constexpr int kMinSegmentTokens = 1024;
-constexpr int kMinSplitTokens = 8192;
-int cu_count() {
-    static int count[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (count[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        count[dev] = n;
-    }
-    return count[dev];
-}
-int choose_segments(int units, int max_seqlen, bool track) {
-    if (track || units <= 0 || max_seqlen < kMinSplitTokens) return 1;
-    int cap = kMaxSegments;
-    if (const char *env = std::getenv("LA_PREFILL_MAX_SEGMENTS")) {
-        const int v = std::atoi(env);
-        cap = v < 1 ? 1 : (v > kMaxSegments ? kMaxSegments : v);
-    }
-    int ns = cu_count() / units;
-    if (ns > cap) ns = cap;
-    if (ns > max_seqlen / kMinSegmentTokens) ns = max_seqlen / kMinSegmentTokens;
-    return ns < 1 ? 1 : ns;
-}
-
-template <int D> hipError_t launch(const PrefillArgs &a, int batch, int max_seqlen, hipStream_t stream) {
+// Launches on `stream`: the chunked kernel alone, or (a.segments > 1, with the
+// caller's workspace in a.seg_ws) the state-only pass, the combine step and
+// the chunked kernel over every segment.
+template <int D> hipError_t launch(const PrefillArgs &a, int batch, hipStream_t stream) {
     PrefillArgs copy = a;
     copy.pairs = batch * a.num_heads;
     const unsigned units = static_cast<unsigned>(copy.pairs) * Geo<D>::NVB;
-    copy.segments = choose_segments(static_cast<int>(units), max_seqlen, a.track_lens != nullptr);
-    copy.seg_ws = nullptr;
     void *args[] = {&copy};
-    if (copy.segments == 1)
-        return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_chunked_kernel<D>), dim3(units), dim3(NT),
-                               args, 0, stream);
-    // sub-segments: enough state-only workgroups to fill the CUs
-    const int per = copy.pairs * (copy.segments - 1);
-    int sub = cu_count() / per;
-    copy.subsegs = sub < 1 ? 1 : (sub > kMaxSubsegs ? kMaxSubsegs : sub);
-    const size_t slices = static_cast<size_t>(per) * copy.subsegs + static_cast<size_t>(copy.pairs) * copy.segments;
-    void *ws = nullptr;
-    hipError_t e = hipMallocAsync(&ws, slices * D * D * sizeof(float), stream);
-    if (e != hipSuccess) {
-        // no workspace (out of memory, no stream-ordered pool): run unsplit
-        (void)hipGetLastError();
+    if (copy.segments <= 1) {
         copy.segments = 1;
         return hipLaunchKernel(reinterpret_cast<const void *>(&prefill_chunked_kernel<D>), dim3(units), dim3(NT),
                                args, 0, stream);
     }
-    copy.seg_ws = static_cast<float *>(ws);
-    e = hipLaunchKernel(reinterpret_cast<const void *>(&prefill_delta_full_kernel<D>),
-                        dim3(static_cast<unsigned>(per * copy.subsegs)), dim3(64 * kDeltaWaves), args, 0, stream);
+    const int per = copy.pairs * (copy.segments - 1);
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&prefill_delta_full_kernel<D>),
+                                   dim3(static_cast<unsigned>(per * copy.subsegs)), dim3(64 * kDeltaWaves), args,
+                                   0, stream);
     if (e == hipSuccess)
         e = hipLaunchKernel(reinterpret_cast<const void *>(&prefill_combine_kernel<D>),
                             dim3(units * kCombineParts), dim3(kCombineThreads), args, 0, stream);
     if (e == hipSuccess)
         e = hipLaunchKernel(reinterpret_cast<const void *>(&prefill_chunked_kernel<D>),
                             dim3(units * copy.segments), dim3(NT), args, 0, stream);
-    const hipError_t f = hipFreeAsync(ws, stream);
-    return e != hipSuccess ? e : f;
+    return e;
 }
 
 }  // namespace
 
-hipError_t launch_prefill_chunked(const PrefillArgs &a, int batch, int head_dim, int max_seqlen,
-                                  hipStream_t stream) {
+hipError_t launch_prefill_chunked(const PrefillArgs &a, int batch, int head_dim, hipStream_t stream) {
     if (batch == 0) return hipSuccess;
-    if (head_dim == 128) return launch<128>(a, batch, max_seqlen, stream);
-    if (head_dim == 64) return launch<64>(a, batch, max_seqlen, stream);
+    if (head_dim == 128) return launch<128>(a, batch, stream);
+    if (head_dim == 64) return launch<64>(a, batch, stream);
     return hipErrorInvalidValue;
 }
 

@@ -74,11 +74,11 @@ def test_slopes_reject_bad_arguments(lib):
 def _prefill(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=la.LA_DTYPE_BF16, cu=FAKE, batch=2, T=10, max_seqlen=8,
              H=4, HK=4, d=128, pool=FAKE, P=4, slot=FAKE, tl=None, ts=None, slopes=FAKE, out=FAKE,
-             stream=None)
+             ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return lib.la_prefill(a["q"], a["k"], a["v"], a["dtype"], a["cu"], a["batch"], a["T"],
                           a["max_seqlen"], a["H"], a["HK"], a["d"], a["pool"], a["P"], a["slot"],
-                          a["tl"], a["ts"], a["slopes"], a["out"], a["stream"])
+                          a["tl"], a["ts"], a["slopes"], a["out"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 def test_prefill_validation(lib):
@@ -110,6 +110,48 @@ def test_prefill_validation(lib):
     # empty work returns before any HIP call
     assert _prefill(lib, batch=0, T=0, max_seqlen=0, q=None, k=None, v=None, out=None, cu=FAKE,
                     slot=None) == la.LA_OK
+    # workspace: NULL only with 0 bytes, 16-byte aligned
+    assert _prefill(lib, ws=None, ws_bytes=64) == E
+    assert _prefill(lib, ws=FAKE + 4, ws_bytes=1 << 30) == E
+
+
+def test_workspace_query_matches_the_documented_size(lib):
+    """la_prefill_workspace_bytes: batch*H*(S + (S-1)*Q) head_dim^2 floats, S
+    segments (as many as fill the compute units, at most 8 and at most
+    max_seqlen/1024), Q sub-segments (as many as fill the compute units, at
+    most 4); 0 when the call would not split (units >= CUs, max_seqlen < 8192)."""
+    q = la.la_prefill_workspace_bytes
+    cus = 256  # MI355X; also the library's fallback without a device
+    for B, T, L, H, d in [(1, 131072, 131072, 8, 128), (1, 16384, 16384, 64, 64), (2, 60000, 40000, 4, 128),
+                          (1, 9000, 9000, 1, 64), (3, 30000, 12000, 2, 128)]:
+        units = B * H * (d // 32)
+        S = min(8, cus // units, L // 1024)
+        if S <= 1:
+            assert q(B, T, L, H, d) == 0
+            continue
+        per = B * H * (S - 1)
+        Q = max(1, min(4, cus // per))
+        assert q(B, T, L, H, d) == (per * Q + B * H * S) * d * d * 4, (B, T, L, H, d)
+    assert q(1, 131072, 131072, 64, 128) == 0      # 256 units fill the GPU
+    assert q(1, 8191, 8191, 8, 128) == 0           # below the split threshold
+    assert q(1, 8192, 8192, 8, 128) > 0
+    assert q(1, 100000, 100000, 8, 96) == 0        # unsupported head_dim
+    assert q(-1, 100000, 100000, 8, 128) == 0
+    assert q(1, -5, 100000, 8, 128) == 0
+
+
+def test_workspace_too_small_is_rejected(lib):
+    """A call that would split into sequence segments rejects a non-NULL
+    workspace smaller than the query's size, before launching anything; a NULL
+    workspace is accepted (the call then runs unsplit, which needs a GPU, so
+    only the rejection is checked here)."""
+    E = la.LA_ERR_INVALID_ARG
+    need = la.la_prefill_workspace_bytes(1, 131072, 131072, 8, 128)
+    assert need > 0
+    kw = dict(batch=1, T=131072, max_seqlen=131072, H=8, HK=8, P=2)
+    assert _prefill(lib, ws=FAKE, ws_bytes=need - 16, **kw) == E
+    assert _prefill(lib, ws=FAKE, ws_bytes=16, **kw) == E
+    assert _prefill(lib, ws=FAKE, ws_bytes=0, **kw) == E
 
 
 def _decode(lib, **kw):

@@ -132,3 +132,36 @@ def test_snapshot_request_on_a_splittable_shape():
     assert_close(pool[1], ref_fin[0], TOL["bf16"], f"{wl.name} final state")
     assert_close(pool[0], ref_snap[0], TOL["bf16"], f"{wl.name} snapshot")
     assert np.array_equal(pool[2].view(np.uint32), wl.pool[2].view(np.uint32)), "untouched slot changed"
+
+
+def test_caller_workspace_exact_size_none_and_too_small():
+    """The split runs in the caller's workspace: a buffer of exactly the queried
+    size (filled with garbage first, so nothing may rely on its contents), a
+    larger one, and no workspace at all (the call then runs unsplit) all match
+    the oracle; a buffer one float short is rejected before anything runs,
+    leaving the pool and the output untouched."""
+    wl = W.make("seg-ws", "prefill", "bf16", 8, [20000], 3, seed=1208, prefix=[True], slot_idx=[2])
+    need = la.la_prefill_workspace_bytes(wl.batch, wl.total_tokens, wl.max_seqlen, wl.num_heads, wl.head_dim)
+    log(f"case {wl.name} T={wl.total_tokens} workspace {need} B")
+    assert need > 0
+    for what, ws in (("exact", torch.full((need // 4,), float("nan"), device="cuda")),
+                     ("larger", torch.full((need // 4 + 1000,), 1e30, device="cuda")),
+                     ("none", None)):
+        dv = device_inputs(wl)
+        out = torch.empty_like(dv["q"])
+        la.la_prefill(dv["q"], dv["k"], dv["v"], dv["cu"], dv["pool"], dv["slot"], dv["slopes"], out,
+                      wl.max_seqlen, workspace=ws)
+        torch.cuda.synchronize()
+        log(f"  workspace {what}")
+        check_against_oracle(wl, out, dv["pool"])
+        check_untouched(wl, dv["pool"])
+    dv = device_inputs(wl)
+    out = torch.full_like(dv["q"], 3.0)
+    short = torch.empty(need // 4 - 1, device="cuda")
+    with pytest.raises(la.LAError) as e:
+        la.la_prefill(dv["q"], dv["k"], dv["v"], dv["cu"], dv["pool"], dv["slot"], dv["slopes"], out,
+                      wl.max_seqlen, workspace=short)
+    assert e.value.status == la.LA_ERR_INVALID_ARG
+    torch.cuda.synchronize()
+    assert torch.all(out.float() == 3.0)
+    assert np.array_equal(dv["pool"].cpu().numpy().view(np.uint32), wl.pool.view(np.uint32))
