@@ -22,6 +22,7 @@ namespace la {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kGroup = 8;  // tokens per decay group of the token-recurrent kernel
 
 // Thread layout for head_dim D: column group cg = tid % CG owns value columns
 // 4cg..4cg+3, row group rg = tid / CG owns key rows RPT*rg .. RPT*rg+RPT-1.
@@ -63,6 +64,29 @@ template <int N> __device__ __forceinline__ void load_n(const float *p, float (&
     }
 }
 
+// N consecutive elements kept as loaded (bf16 stays packed, two per register)
+// and converted where they are used.
+template <typename T, int N> struct Row;
+template <int N> struct Row<uint16_t, N> {
+    static_assert(N == 4 || N % 8 == 0, "4 or a multiple of 8 elements");
+    static constexpr int W = N == 4 ? 4 : 8;  // elements per load
+    typedef uint16_t vec __attribute__((ext_vector_type(W)));
+    vec x[N / W];
+    __device__ void load(const uint16_t *p) {
+#pragma unroll
+        for (int i = 0; i < N / W; ++i) x[i] = *reinterpret_cast<const vec *>(p + W * i);
+    }
+    __device__ float operator[](int r) const { return bf16_to_f32(x[r / W][r % W]); }
+};
+template <int N> struct Row<float, N> {
+    f32x4 x[N / 4];
+    __device__ void load(const float *p) {
+#pragma unroll
+        for (int i = 0; i < N / 4; ++i) x[i] = *reinterpret_cast<const f32x4 *>(p + 4 * i);
+    }
+    __device__ float operator[](int r) const { return x[r / 4][r % 4]; }
+};
+
 __device__ __forceinline__ f32x4 load4(const uint16_t *p) {
     u16x4 a = *reinterpret_cast<const u16x4 *>(p);
     return f32x4{bf16_to_f32(a[0]), bf16_to_f32(a[1]), bf16_to_f32(a[2]), bf16_to_f32(a[3])};
@@ -91,12 +115,12 @@ __device__ __forceinline__ void store_state(float *s, int soff, const f32x4 (&S)
         __builtin_nontemporal_store(S[r], reinterpret_cast<f32x4 *>(s + soff + r * D));
 }
 
-// o = scale * q @ S for this thread's columns, summed over all row groups and
+// o = oscale * q @ S for this thread's columns, summed over all row groups and
 // stored by wave 0.  red is double-buffered by `parity`, so one barrier per
 // token suffices: a buffer is rewritten only after the next barrier.
 template <int D, typename T>
 __device__ __forceinline__ void reduce_store(f32x4 o, f32x4 (&red)[2][4][Layout<D>::CG], int &parity,
-                                             T *dst) {
+                                             T *dst, float oscale = Layout<D>::kScale) {
     using L = Layout<D>;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, cg = tid % L::CG;
 #pragma unroll
@@ -111,7 +135,7 @@ __device__ __forceinline__ void reduce_store(f32x4 o, f32x4 (&red)[2][4][Layout<
     if (wave == 0 && lane < L::CG) {
         const f32x4 s = red[parity][0][lane] + red[parity][1][lane] + red[parity][2][lane] +
                         red[parity][3][lane];
-        store4(dst + 4 * lane, s * L::kScale);
+        store4(dst + 4 * lane, s * oscale);
     }
     parity ^= 1;
 }
@@ -132,8 +156,10 @@ __device__ __forceinline__ void decay_step(f32x4 &x, float dhi, f32x4 t) {
     for (int i = 0; i < 4; ++i) asm("v_fma_f32 %0, %1, %0, %2" : "+v"(x[i]) : "v"(dhi), "v"(t[i]));
 }
 
-// kTrack: the prefill variant that may take a state-tracking snapshot
-template <typename T, int D, bool kTrack>
+// kTrack: the prefill variant that may take a state-tracking snapshot.
+// kMulti: requests of more than one token (without it every token is a group
+// of its own: decode, whose one-token body then needs fewer registers).
+template <typename T, int D, bool kTrack, bool kMulti>
 __global__ __launch_bounds__(kThreads) void recurrent_kernel(RecurrentArgs a) {
     using L = Layout<D>;
     constexpr int RPT = L::RPT;
@@ -182,42 +208,66 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(RecurrentArgs a) {
 
     f32x4 S[RPT];
     load_state<D>(s_in, soff, S);
-    // fp32 inputs carry the decay e^{-l} as an unevaluated float pair
-    // dhi + dlo, every step rounded once: S <- round(dhi S + (dlo S + k v)).
-    // A single float factor misstates the decay rate by up to 2^-25 / l
-    // relative, and rounding S + (e^{-l} - 1) S on its own loses or doubles a
-    // decay below half an ulp of S every step; both compound over a request's
-    // tokens and over successive calls, which the fp32 bound of 1e-4 does not
-    // absorb for small slopes and long requests.  dlo comes from expm1f:
-    // e^{-l} - dhi = (1 - dhi) + expm1(-l), where 1 - dhi is exact.  bf16
-    // inputs keep the single factor (rate error below 1.2e-4 relative for
-    // l >= 2^-12): the pair's extra multiply per element and token costs
-    // chain verify ~13%.
-    constexpr bool kPair = std::is_same<T, float>::value;
+    // Decay arithmetic.  Multiplying the state by fl(e^{-l}) at every token
+    // compounds the factor's rounding over a request and over successive
+    // calls: the decay rate is off by up to 2^-25 / l relative (1.53x at
+    // l = 3.9e-8, the slope of a last layer).  Here the tokens go in groups
+    // of up to kGroup; with e the group's last token, the group runs in the
+    // frame Y_s = e^{-l(e-s)} S_s:
+    //   first token t:  Y <- round(whi S + (wlo S + w_t k_t v_t^T))
+    //   later tokens:   Y <- Y + w_s k_s v_s^T,   w_s = e^{-l(e-s)} <= 1
+    //   outputs:        o_s = scale e^{l(e-s)} q_s Y_s
+    // and Y_e = S_e.  The group's decay e^{-l G} is the float pair whi + wlo
+    // (wlo = expm1(-l G) - (whi - 1), whi - 1 exact), applied in the same
+    // rounding as the first update, so the state decays at the exact rate
+    // wherever the updates randomize the rounding, and each token costs two
+    // operations per state element instead of three.  (Where they do not --
+    // |S| < 256 |k v| for bf16 inputs, whose products lie on a grid no finer
+    // than the state's ulp -- a sub-ulp decay per group rounds to a whole
+    // number of ulps, and no round-to-nearest update is exact.)  The output
+    // factor e^{l(e-s)} is kept below e^32 by the group length.
     const float lam = a.slopes[h];
-    const float dhi = expf(-lam);
-    const float dlo = kPair && dhi >= 0.5f ? (1.f - dhi) + expm1f(-lam) : 0.f;
+    const float alam = fabsf(lam);
+    int gmax = kMulti ? kGroup : 1;
+    if (kMulti && !(alam * (kGroup - 1) <= 32.f)) gmax = alam <= 32.f ? 1 + static_cast<int>(32.f / alam) : 1;
 
     __shared__ f32x4 red[2][4][L::CG];
     int parity = 0;
-    for (int64_t t = t0; t < t1; ++t) {
-        if (kTrack && snap && t - t0 == tl) store_state<D>(snap, soff, S);
-        const size_t off = t * row + static_cast<size_t>(h) * D;
-        const size_t kvoff = t * kvrow + static_cast<size_t>(hk) * D;
-        float kk[RPT], qq[RPT];
-        load_n<RPT>(k + kvoff + RPT * rg, kk);
-        load_n<RPT>(q + off + RPT * rg, qq);
+    // one token; kFirst: the first of its group, which also applies the decay
+    auto token = [&](int64_t s, int64_t e, float whi, float wlo, auto first) {
+        constexpr bool kFirst = decltype(first)::value;
+        const float w = expf(-lam * static_cast<float>(e - s));
+        const size_t off = s * row + static_cast<size_t>(h) * D;
+        const size_t kvoff = s * kvrow + static_cast<size_t>(hk) * D;
+        Row<T, RPT> kk, qq;
+        kk.load(k + kvoff + RPT * rg);
+        qq.load(q + off + RPT * rg);
         const f32x4 vv = load4(v + kvoff + 4 * cg);
         f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < RPT; ++r) {
-            if constexpr (kPair)
-                decay_step(S[r], dhi, dlo * S[r] + kk[r] * vv);
+            if constexpr (kFirst)
+                decay_step(S[r], whi, wlo * S[r] + (w * kk[r]) * vv);
             else
-                S[r] = dhi * S[r] + kk[r] * vv;
+                S[r] += (w * kk[r]) * vv;
             o += qq[r] * S[r];
         }
-        reduce_store<D>(o, red, parity, out + off);
+        reduce_store<D>(o, red, parity, out + off, L::kScale * expf(lam * static_cast<float>(e - s)));
+    };
+    for (int64_t t = t0; t < t1;) {
+        int64_t G = t1 - t < gmax ? t1 - t : gmax;
+        if (kTrack && snap) {
+            // groups end at the snapshot point, where the frame is the state
+            if (t - t0 == tl) store_state<D>(snap, soff, S);
+            if (t - t0 < tl && tl - (t - t0) < G) G = tl - (t - t0);
+        }
+        const int64_t e = t + G - 1;
+        const float whi = expf(-lam * static_cast<float>(G));
+        const float wlo = whi >= 0.5f ? expm1f(-lam * static_cast<float>(G)) - (whi - 1.f) : 0.f;
+        token(t, e, whi, wlo, std::true_type{});
+        if constexpr (kMulti)
+            for (int64_t s = t + 1; s <= e; ++s) token(s, e, whi, wlo, std::false_type{});
+        t = e + 1;
     }
     if (kTrack && snap && tl == t1 - t0) store_state<D>(snap, soff, S);
     store_state<D>(s_out, soff, S);
@@ -266,11 +316,11 @@ __global__ __launch_bounds__(kThreads) void tree_kernel(TreeArgs a) {
     const int soff = (RPT * rg) * D + 4 * cg;
     const float *R = a.pool + (static_cast<size_t>(slot) * H + h) * sdd + soff;
     f32x4 A[RPT];
-    // decay as in recurrent_kernel: a float pair for fp32 inputs
-    constexpr bool kPair = std::is_same<T, float>::value;
+    // Decay as a float pair dhi + dlo (see recurrent_kernel): every draft
+    // state may become the request's next state.
     const float lam = a.slopes[h];
     const float dhi = expf(-lam);
-    const float dlo = kPair && dhi >= 0.5f ? (1.f - dhi) + expm1f(-lam) : 0.f;
+    const float dlo = dhi >= 0.5f ? (1.f - dhi) + expm1f(-lam) : 0.f;
 
     auto kv = [&](int j, float (&kk)[RPT], f32x4 &vv) {
         const size_t kvoff = (t0 + j) * kvrow + static_cast<size_t>(hk) * D;
@@ -289,24 +339,21 @@ __global__ __launch_bounds__(kThreads) void tree_kernel(TreeArgs a) {
         const int p = par[j];
         if (p >= 0 && p == j - 1) {
 #pragma unroll
-            for (int r = 0; r < RPT; ++r) {
-                if constexpr (kPair)
-                    decay_step(A[r], dhi, dlo * A[r] + kk[r] * vv);
-                else
-                    A[r] = dhi * A[r] + kk[r] * vv;
-            }
+            for (int r = 0; r < RPT; ++r) decay_step(A[r], dhi, dlo * A[r] + kk[r] * vv);
         } else if (p < 0) {
 #pragma unroll
             for (int r = 0; r < RPT; ++r) {
                 const f32x4 root = *reinterpret_cast<const f32x4 *>(R + r * D);
-                A[r] = kPair ? dhi * root + (dlo * root + kk[r] * vv) : dhi * root + kk[r] * vv;
+                A[r] = dhi * root + (dlo * root + kk[r] * vv);
             }
         } else {
 #pragma unroll
             for (int r = 0; r < RPT; ++r) A[r] = kk[r] * vv;
             // the weight of an ancestor m steps up is dhi^m (m <= num_draft, so
-            // the factor's rounding stays below m 2^-25)
+            // the factor's rounding stays below m 2^-25, once per call); the
+            // root's weight e^{-l depth} is a pair whi + wlo, as for one step
             float w = dhi;
+            int depth = 1;
             for (int x = p; x >= 0; x = par[x]) {
                 float ka[RPT];
                 f32x4 va;
@@ -314,9 +361,16 @@ __global__ __launch_bounds__(kThreads) void tree_kernel(TreeArgs a) {
 #pragma unroll
                 for (int r = 0; r < RPT; ++r) A[r] += (w * ka[r]) * va;
                 w *= dhi;
+                ++depth;
             }
+            // e^{-l depth} - w = expm1(-l depth) - (w - 1), with w - 1 exact for
+            // w >= 1/2 (below that the rate error of w alone is negligible)
+            const float wlo = dlo == 0.f || w < 0.5f ? 0.f : expm1f(-lam * static_cast<float>(depth)) - (w - 1.f);
 #pragma unroll
-            for (int r = 0; r < RPT; ++r) A[r] += w * *reinterpret_cast<const f32x4 *>(R + r * D);
+            for (int r = 0; r < RPT; ++r) {
+                const f32x4 root = *reinterpret_cast<const f32x4 *>(R + r * D);
+                A[r] += w * root + wlo * root;
+            }
         }
         f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -331,8 +385,10 @@ template <typename T, int D>
 hipError_t launch_rec(const RecurrentArgs &a, int batch, hipStream_t stream) {
     RecurrentArgs copy = a;
     void *args[] = {&copy};
-    const void *fn = a.track_lens ? reinterpret_cast<const void *>(&recurrent_kernel<T, D, true>)
-                                  : reinterpret_cast<const void *>(&recurrent_kernel<T, D, false>);
+    const bool one = !a.cu_seqlens && a.tokens_per_req == 1;  // decode
+    const void *fn = a.track_lens ? reinterpret_cast<const void *>(&recurrent_kernel<T, D, true, true>)
+                     : one        ? reinterpret_cast<const void *>(&recurrent_kernel<T, D, false, false>)
+                                  : reinterpret_cast<const void *>(&recurrent_kernel<T, D, false, true>);
     return hipLaunchKernel(fn,
                            dim3(static_cast<unsigned>(batch) * a.num_heads), dim3(kThreads), args,
                            0, stream);

@@ -1,0 +1,123 @@
+"""The decay rate of repeated bf16 decode and in-place chain-verify calls at
+the smallest layer-scaled slope.
+
+The slope bullet of [LA-page] §独立参考实现 scales the ALiBi slopes by
+1 - layer_id/(L-1) + 1e-5, so a model's last layer has slopes near
+2^-8 * 1e-5 ~ 3.9e-8.  The nearest float to e^{-l} is then 1 - 2^-24, which
+decays at 1.53x the intended rate; the kernels carry the decay as a float
+pair instead, rounding each step once.  Each call starts from the fp32 state in the pool, so a rate
+error compounds over calls.
+
+What an fp32 state can hold depends on the update k v^T.  Products of two
+bf16 values lie on a grid of 2^-15 of their magnitude; while |S| < 256 |k v|
+that grid is no finer than the state's ulp, every step's rounding is decided
+by the sub-ulp decay alone, and no round-to-nearest form of the step gives
+the exact rate (a per-step decay of 0.3-0.7 ulp rounds to 0 or 1 ulp).  Where
+|S| >> 256 |k v| the update lands at effectively random positions within an
+ulp, the rounding is unbiased, and the pair must reproduce e^{-l n} exactly.
+
+Both regimes are checked against the fp64 oracle over 1000 decode steps and
+200 verify calls of 5 drafts:
+  * |S| ~ 1e4: effective rate within 2% of the slope, final states within
+    5e-6 relative rms of the oracle (a single float factor: 1.54x, 2.1e-5);
+  * |S| ~ 30: effective rate within [0.6, 1.4] of the slope (measured in an
+    fp32 emulation of the same steps: 0.74 for the pair, 1.97 for a single
+    float factor).
+The effective rate is read off two requests with identical k, v and
+different initial states A and 0: their final states differ by w A with
+w = e^{-l_eff n}.
+"""
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_amd as la
+import oracle
+from linear_attention_amd.workloads import bf16_round_bits
+
+from gpu_util import dev_io, log
+
+pytestmark = pytest.mark.gpu
+
+LAM = np.float32(2.0 ** -8 * 1e-5)  # the last layer's smallest slope
+H, D = 2, 128
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    la.load()
+
+
+def _inputs(seed, steps, amp):
+    """Request 0 starts from A = amp * N(0,1), request 1 from zero; both see the
+    same k, v at every step (q differs, it does not touch the state)."""
+    rng = np.random.default_rng(seed)
+    kv = [bf16_round_bits(rng.standard_normal((steps, 1, H, D), dtype=np.float32)) for _ in range(2)]
+    k, v = (np.ascontiguousarray(np.repeat(x, 2, axis=1)) for x in kv)      # [steps, 2, H, D]
+    q = bf16_round_bits(rng.standard_normal((steps, 2, H, D), dtype=np.float32))
+    pool = np.zeros((3, H, D, D), dtype=np.float32)
+    pool[2] = (amp * rng.standard_normal((H, D, D))).astype(np.float32)
+    slot = np.array([2, 0], dtype=np.int32)
+    return q, k, v, pool, slot
+
+
+def _oracle_final(q, k, v, pool, slot):
+    steps = q.shape[0]
+    tok = lambda x: np.ascontiguousarray(x.transpose(1, 0, 2, 3).reshape(2 * steps, H, D))  # noqa: E731
+    cu = np.array([0, steps, 2 * steps])
+    slopes = np.full(H, LAM, dtype=np.float32)
+    _, fin = oracle.run(tok(q), tok(k), tok(v), cu, pool[slot], slopes)
+    return fin
+
+
+def _run(kind, q, k, v, pool, slot):
+    dq, dk, dv = dev_io(q, "bf16"), dev_io(k, "bf16"), dev_io(v, "bf16")
+    dpool = torch.from_numpy(pool).cuda()
+    dslot = torch.from_numpy(slot).cuda()
+    slopes = torch.full((H,), float(LAM), dtype=torch.float32, device="cuda")
+    steps = q.shape[0]
+    if kind == "decode":
+        out = torch.empty_like(dq[0])
+        for t in range(steps):
+            la.la_decode(dq[t], dk[t], dv[t], dpool, dslot, slopes, out)
+    else:
+        nd = 5
+        out = torch.empty((2 * nd, H, D), dtype=torch.bfloat16, device="cuda")
+        for c in range(steps // nd):
+            blk = lambda x: x[c * nd:(c + 1) * nd].transpose(0, 1).reshape(2 * nd, H, D).contiguous()  # noqa: E731
+            la.la_verify(blk(dq), blk(dk), blk(dv), nd, dpool, dslot, slopes, out, None)
+    torch.cuda.synchronize()
+    return dpool[slot.astype(np.int64)].cpu().numpy().astype(np.float64)
+
+
+def _rate(fin, A, steps):
+    w = float(((fin[0] - fin[1]) * A).sum() / (A.astype(np.float64) ** 2).sum())
+    return (1.0 - w) / (float(LAM) * steps)
+
+
+@pytest.mark.parametrize("kind", ["decode", "verify"])
+def test_exact_rate_where_rounding_is_unbiased(kind):
+    steps = 1000
+    q, k, v, pool, slot = _inputs(2100, steps, amp=1e4)
+    log(f"decay-rate {kind}: {steps} steps, slope {LAM:.3e}, |S| ~ 1e4")
+    got = _run(kind, q, k, v, pool, slot)
+    ref = _oracle_final(q, k, v, pool, slot)
+    rate = _rate(got, pool[2], steps)
+    rms = float(np.sqrt(((got - ref) ** 2).mean() / (ref ** 2).mean()))
+    log(f"  effective rate / slope = {rate:.4f}  (oracle: {_rate(ref, pool[2], steps):.4f}); "
+        f"final-state rms rel error {rms:.2e}")
+    assert abs(rate - 1.0) < 0.02
+    assert rms < 5e-6
+
+
+@pytest.mark.parametrize("kind", ["decode", "verify"])
+def test_bounded_rate_where_rounding_is_decided_by_the_decay(kind):
+    steps = 1000
+    q, k, v, pool, slot = _inputs(2200, steps, amp=30.0)
+    log(f"decay-rate {kind}: {steps} steps, slope {LAM:.3e}, |S| ~ 30")
+    got = _run(kind, q, k, v, pool, slot)
+    rate = _rate(got, pool[2], steps)
+    log(f"  effective rate / slope = {rate:.4f}")
+    assert 0.6 < rate < 1.4
