@@ -81,7 +81,7 @@ def to_f64(x: np.ndarray) -> np.ndarray:
     if x.dtype == np.uint16:
         return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
     if x.dtype in (np.float32, np.float64):
-        return x.astype(np.float64)
+        return x.astype(np.float64, copy=False)
     raise TypeError(f"unsupported oracle input dtype {x.dtype}")
 
 

@@ -50,17 +50,18 @@ def test_config5_chain_verify_state_out():
     _full_check(W.config(5), state_out=True)
 
 
-def test_config4_long_prefill_sampled_heads():
-    """Full 131072-token request at H=64; the oracle checks every token of a
-    sample of heads covering the largest, a middle and the smallest slope."""
+def test_config4_long_prefill_all_heads():
+    """The full 131072-token request at H=64: every output and the final state
+    of every head against the oracle, eight heads at a time (so that only one
+    group is upcast to fp64 on the host at once)."""
     wl = W.config(4)
-    log(f"case {wl.name} T={wl.total_tokens}")
+    log(f"case {wl.name} T={wl.total_tokens} H={wl.num_heads}")
     out, pool, _ = run_gpu(wl)
-    heads = [0, 37, 63]
-    check_against_oracle(wl, out, pool, heads=heads)
+    for g in range(0, wl.num_heads, 8):
+        heads = list(range(g, g + 8))
+        log(f"  heads {heads[0]}..{heads[-1]}")
+        check_against_oracle(wl, out, pool, heads=heads)
     check_untouched(wl, pool)
-    o = out.float()
-    assert torch.isfinite(o).all()
 
 
 EDGE_LENGTHS = [1, 63, 64, 65, 0, 131, 2, 200, 127, 128, 129]

@@ -18,7 +18,7 @@ import oracle
 from linear_attention_amd import workloads as W
 
 from gpu_util import (TOL, assert_close, check_against_oracle, check_untouched, device_inputs,
-                      host_io, log, run_gpu, to_f64)
+                      host_io, log, oracle_ref, run_gpu, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -360,19 +360,28 @@ def test_graph_capture_replay_decode_and_verify():
     """Decode, chain verify and tree verify captured in one HIP graph
     ([LA-page] §生产环境不支持 item 2: graph capture covers the decode and
     target-verify modes) and replayed several times, with eager work between
-    replays; every replay matches the eager results bit for bit."""
+    replays.  Every replay's outputs, pool and states match the fp64 oracle
+    within the bf16 bound, and the eager run bit for bit."""
     dec = W.make("graph-decode", "decode", "bf16", 8, np.ones(6, dtype=np.int64), 16, seed=800,
                  fill_all_slots=True)
     ver = W.make("graph-verify", "verify", "bf16", 8, np.full(4, 3, dtype=np.int64), 8, seed=801,
                  prefix=np.ones(4, dtype=bool), num_draft=3, num_kv_heads=2)
     dd, dv = device_inputs(dec), device_inputs(ver)
     pool0 = dd["pool"].clone()
-    parents = i32(np.tile(np.array([-1, 0, 0], dtype=np.int32), (4, 1)))
+    par_np = np.tile(np.array([-1, 0, 0], dtype=np.int32), (4, 1))
+    parents = i32(par_np)
     out_d = torch.empty_like(dd["q"])
     out_v = torch.empty_like(dv["q"])
     out_t = torch.empty_like(dv["q"])
     so = torch.empty((4, 8, 128, 128), device="cuda")
     ds = torch.empty((4, 3, 8, 128, 128), device="cuda")
+
+    # the oracle's results for one step from the initial pools
+    tol = TOL["bf16"]
+    ref_d_out, ref_d_fin = oracle_ref(dec)
+    ref_d_pool = oracle.scatter(dec.pool, dec.slot_idx, ref_d_fin)
+    ref_v_out, ref_v_fin = oracle_ref(ver)
+    ref_t_out, ref_t_states = _oracle_tree(ver, par_np)
 
     def step():
         la.la_decode(dd["q"], dd["k"], dd["v"], dd["pool"], dd["slot"], dd["slopes"], out_d)
@@ -380,8 +389,17 @@ def test_graph_capture_replay_decode_and_verify():
         la.la_verify_tree(dv["q"], dv["k"], dv["v"], 3, dv["pool"], dv["slot"], parents, dv["slopes"],
                           out_t, ds)
 
+    def check_oracle(what):
+        assert_close(host_io(out_d), ref_d_out, tol, f"{what} decode out")
+        assert_close(dd["pool"].cpu().numpy(), ref_d_pool, tol, f"{what} decode pool")
+        assert_close(host_io(out_v), ref_v_out, tol, f"{what} verify out")
+        assert_close(so.cpu().numpy(), ref_v_fin, tol, f"{what} verify state")
+        assert_close(host_io(out_t), ref_t_out, tol, f"{what} tree out")
+        assert_close(ds.cpu().numpy(), ref_t_states, tol, f"{what} tree states")
+
     step()
     torch.cuda.synchronize()
+    check_oracle("eager")
     ref = [t.clone() for t in (out_d, dd["pool"], out_v, so, out_t, ds)]
 
     dd["pool"].copy_(pool0)
@@ -400,6 +418,7 @@ def test_graph_capture_replay_decode_and_verify():
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
+        check_oracle(f"replay {rep}")
         got = (out_d, dd["pool"], out_v, so, out_t, ds)
         for name, a, b in zip(("decode out", "decode pool", "verify out", "verify state", "tree out",
                                "tree states"), got, ref):

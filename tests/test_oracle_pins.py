@@ -241,3 +241,27 @@ def test_alibi_power_of_two_ratio(H):
     if H > 1:
         np.testing.assert_allclose(s[1:] / s[:-1], r, rtol=2e-7)
     np.testing.assert_allclose(s[-1], 2.0 ** -8, rtol=1e-7)
+
+
+def test_bf16_upcast_matches_torch_on_every_bit_pattern():
+    """oracle.to_f64 reads uint16 arrays as bfloat16 bit patterns.  Every one of
+    the 65536 patterns (both zeros, subnormals, the largest finite values,
+    infinities, NaNs, and the patterns on either side of every rounding tie)
+    must upcast to exactly what torch's own bfloat16 -> float64 conversion
+    gives; a shifted, sign-dropping or truncating upcast fails here."""
+    import torch
+
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = oracle.to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint64), ref[~nan].view(np.uint64))  # -0.0 stays -0.0
+    # spot values fixed by the format: sign bit, exponent bias 127, 7 mantissa bits
+    assert got[0x3F80] == 1.0 and got[0xBF80] == -1.0 and got[0x4000] == 2.0
+    assert got[0x0001] == 2.0 ** -133                    # smallest subnormal
+    assert got[0x7F7F] == (2 - 2 ** -7) * 2.0 ** 127     # largest finite
+    assert got[0x7F80] == np.inf and got[0xFF80] == -np.inf
+    # float32 and float64 inputs pass through unchanged
+    x = np.array([1.5, -0.0, 3e-39, np.float32(1e38)], dtype=np.float32)
+    assert np.array_equal(oracle.to_f64(x).view(np.uint64), x.astype(np.float64).view(np.uint64))
