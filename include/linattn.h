@@ -74,7 +74,8 @@ typedef enum {
     LA_OK = 0,
     LA_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad metadata (LA_DEBUG) */
     LA_ERR_UNSUPPORTED = -2, /* head_dim not 64/128, unknown dtype, num_draft <= 0 */
-    LA_ERR_HIP = -3          /* a HIP runtime call or kernel launch failed */
+    LA_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed */
+    LA_ERR_NO_SCRATCH = -4   /* la_prefill_noalloc: the split needs more than its static scratch */
 } la_status;
 
 typedef enum {
@@ -165,6 +166,29 @@ la_status la_prefill(const void *q, const void *k, const void *v, la_dtype dtype
                      const int32_t *track_lens, const int32_t *track_slot_idx,
                      const float *slopes, void *out, void *workspace, size_t workspace_bytes,
                      hipStream_t stream);
+
+/*
+ * la_prefill for callers that cannot allocate or own device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments, semantics and errors as la_prefill without the workspace:
+ * a call that splits into sequence segments takes its scratch from a static
+ * device array of LA_NOALLOC_SCRATCH_BYTES bytes that the library holds on
+ * every GPU it runs on until the process ends.  No allocation, no host
+ * synchronisation.  A split that needs more scratch than that (never on a
+ * 256-CU MI355X, whose largest split needs 18 MiB) returns
+ * LA_ERR_NO_SCRATCH before anything is launched.
+ * All calls on one GPU share its array: calls that overlap on one GPU (on
+ * different streams, or concurrently from several host threads) race.  Each
+ * call writes every part of the array it later reads, so nothing needs
+ * clearing between calls.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES (32u << 20)
+la_status la_prefill_noalloc(const void *q, const void *k, const void *v, la_dtype dtype,
+                             const int32_t *cu_seqlens, int batch, int64_t total_tokens, int max_seqlen,
+                             int num_heads, int num_kv_heads, int head_dim,
+                             float *state_pool, int64_t pool_slots, const int32_t *slot_idx,
+                             const int32_t *track_lens, const int32_t *track_slot_idx,
+                             const float *slopes, void *out, hipStream_t stream);
 
 /*
  * Decode: one token per request (q, out are [batch, H, d]; k, v [batch, Hkv, d]).

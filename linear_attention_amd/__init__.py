@@ -21,11 +21,11 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liblinattn.so")
 
-LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, -1, -2, -3
+LA_OK, LA_ERR_INVALID_ARG, LA_ERR_UNSUPPORTED, LA_ERR_HIP, LA_ERR_NO_SCRATCH = 0, -1, -2, -3, -4
 LA_DTYPE_BF16, LA_DTYPE_F32 = 0, 1
 
 EXPORTED = ("la_status_string", "la_alibi_slopes", "la_prefill_workspace_bytes", "la_prefill",
-            "la_decode", "la_verify", "la_verify_tree")
+            "la_prefill_noalloc", "la_decode", "la_verify", "la_verify_tree")
 
 _lib = None
 
@@ -55,6 +55,8 @@ def load():
     lib.la_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.la_prefill.argtypes = [P, P, P, I, P, I, L, I, I, I, I, P, L, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.la_prefill.restype = I
+    lib.la_prefill_noalloc.argtypes = [P, P, P, I, P, I, L, I, I, I, I, P, L, P, P, P, P, P, P]
+    lib.la_prefill_noalloc.restype = I
     lib.la_decode.argtypes = [P, P, P, I, I, I, I, I, P, L, P, P, P, P]
     lib.la_decode.restype = I
     lib.la_verify.argtypes = [P, P, P, I, I, I, I, I, I, P, L, P, P, P, P, P]
@@ -202,6 +204,36 @@ def la_prefill(q, k, v, cu_seqlens, state_pool, slot_idx, slopes, out, max_seqle
                            _ptr(slopes, "slopes", (torch.float32,)), _ptr(out, "out", io),
                            ws_ptr, ws_bytes, _stream(state_pool, stream))
     _check(rc, "la_prefill")
+
+
+def la_prefill_noalloc(q, k, v, cu_seqlens, state_pool, slot_idx, slopes, out, max_seqlen,
+                       track_lens=None, track_slot_idx=None, stream=None):
+    """la_prefill without a workspace, for callers that cannot allocate: a split
+    into sequence segments uses the library's static per-GPU scratch (calls
+    that overlap on one GPU race).  Arguments as for la_prefill."""
+    import torch
+
+    io = (torch.bfloat16, torch.float32)
+    T, H, HK, d = _qkv_shapes(q, k, v, out, "T")
+    B = cu_seqlens.numel() - 1
+    if slot_idx.numel() != B:
+        raise ValueError("slot_idx must have one entry per request")
+    if (track_lens is None) != (track_slot_idx is None):
+        raise ValueError("track_lens and track_slot_idx go together")
+    if track_lens is not None and (track_lens.numel() != B or track_slot_idx.numel() != B):
+        raise ValueError("track arrays must have one entry per request")
+    _pool_and_slopes(state_pool, slopes, H, d, q, k, v, out, cu_seqlens, slot_idx, track_lens, track_slot_idx)
+    i32 = (torch.int32,)
+    with torch.cuda.device(state_pool.device):
+        rc = load().la_prefill_noalloc(_ptr(q, "q", io), _ptr(k, "k", io), _ptr(v, "v", io), _io_dtype(q),
+                                       _ptr(cu_seqlens, "cu_seqlens", i32), B, T, int(max_seqlen), H, HK, d,
+                                       _ptr(state_pool, "state_pool", (torch.float32,)), state_pool.shape[0],
+                                       _ptr(slot_idx, "slot_idx", i32, True),
+                                       _ptr(track_lens, "track_lens", i32, True),
+                                       _ptr(track_slot_idx, "track_slot_idx", i32, True),
+                                       _ptr(slopes, "slopes", (torch.float32,)), _ptr(out, "out", io),
+                                       _stream(state_pool, stream))
+    _check(rc, "la_prefill_noalloc")
 
 
 def la_decode(q, k, v, state_pool, slot_idx, slopes, out, stream=None):

@@ -7,6 +7,7 @@
 
 #include <atomic>
 #include <cstdlib>
+#include <mutex>
 #include <vector>
 
 #include "host_logic.h"
@@ -15,6 +16,13 @@
 
 using la::aligned16;
 using la::common_checks;
+
+// Scratch of la_prefill_noalloc: a file-scope device array, one copy per GPU.
+// In host code `scratch` only names the symbol; the device address of each
+// GPU's copy comes from hipGetSymbolAddress, taken once per device with that
+// device current, and only that address is handed to kernels.
+static_assert(LA_NOALLOC_SCRATCH_BYTES % 256 == 0, "whole 256-byte blocks");
+static __device__ __align__(256) float scratch[LA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
 
 namespace {
 
@@ -71,6 +79,23 @@ int segment_cap() {
     return cap < 1 ? 1 : (cap > la::kMaxSegments ? la::kMaxSegments : cap);
 }
 
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void *scratch_addr[kMaxDevices];
+
+// The current device's copy of `scratch`, or null if its address cannot be had.
+void *scratch_on_current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_addr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        scratch_addr[dev] = ptr;
+    }
+    return scratch_addr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -81,6 +106,8 @@ const char *la_status_string(la_status s) {
     case LA_ERR_INVALID_ARG: return "LA_ERR_INVALID_ARG: invalid argument";
     case LA_ERR_UNSUPPORTED: return "LA_ERR_UNSUPPORTED: unsupported configuration";
     case LA_ERR_HIP: return "LA_ERR_HIP: HIP runtime error";
+    case LA_ERR_NO_SCRATCH:
+        return "LA_ERR_NO_SCRATCH: the prefill split needs more than the static scratch (LA_NOALLOC_SCRATCH_BYTES)";
     }
     return "unknown la_status";
 }
@@ -162,6 +189,27 @@ la_status la_prefill(const void *q, const void *k, const void *v, la_dtype dtype
     a.slopes = slopes;
     a.out = out;
     return from_hip(la::launch_recurrent(a, dtype == LA_DTYPE_BF16, head_dim, batch, stream));
+}
+
+la_status la_prefill_noalloc(const void *q, const void *k, const void *v, la_dtype dtype,
+                             const int32_t *cu_seqlens, int batch, int64_t total_tokens, int max_seqlen,
+                             int num_heads, int num_kv_heads, int head_dim, float *state_pool,
+                             int64_t pool_slots, const int32_t *slot_idx, const int32_t *track_lens,
+                             const int32_t *track_slot_idx, const float *slopes, void *out,
+                             hipStream_t stream) {
+    la_status st = common_checks(q, k, v, dtype, total_tokens, batch, num_heads, num_kv_heads,
+                                 head_dim, state_pool, pool_slots, slot_idx, slopes, out);
+    if (st != LA_OK) return st;
+    if (max_seqlen < 0 || (batch > 0 && !cu_seqlens)) return LA_ERR_INVALID_ARG;
+    void *ws = scratch_on_current_device();
+    if (!ws) return LA_ERR_HIP;
+    if (dtype == LA_DTYPE_BF16 && batch > 0 && !track_lens && max_seqlen >= la::kMinSplitTokens &&
+        la::plan_segments(cu_count(), batch, num_heads, head_dim, max_seqlen, false, segment_cap())
+                .workspace_bytes > LA_NOALLOC_SCRATCH_BYTES)
+        return LA_ERR_NO_SCRATCH;
+    return la_prefill(q, k, v, dtype, cu_seqlens, batch, total_tokens, max_seqlen, num_heads, num_kv_heads,
+                      head_dim, state_pool, pool_slots, slot_idx, track_lens, track_slot_idx, slopes, out, ws,
+                      LA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 la_status la_decode(const void *q, const void *k, const void *v, la_dtype dtype, int batch,

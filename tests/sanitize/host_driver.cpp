@@ -78,6 +78,17 @@ int main() {
                                 CHECK(pl.workspace_bytes == slices * d * d * sizeof(float));
                             }
 
+    // on a 256-CU part every split fits the static scratch of la_prefill_noalloc
+    size_t most = 0;
+    for (int batch = 1; batch <= 64; ++batch)
+        for (int H = 1; H <= 64; ++H)
+            for (int d : {64, 128}) {
+                const SegmentPlan pl = plan_segments(256, batch, H, d, 1 << 20, false, kMaxSegments);
+                most = pl.workspace_bytes > most ? pl.workspace_bytes : most;
+            }
+    CHECK(most > 0 && most <= LA_NOALLOC_SCRATCH_BYTES);
+    std::printf("largest split workspace on 256 CUs: %zu bytes\n", most);
+
     // metadata checks
     const int32_t cu_ok[4] = {0, 3, 3, 10}, cu_dec[4] = {0, 5, 4, 10}, cu_big[4] = {0, 3, 3, 2147483647};
     const int32_t slots[3] = {2, 0, 5}, dup[3] = {2, 0, 2}, neg[3] = {2, -1, 5}, far[3] = {2, 0, 2147483647};

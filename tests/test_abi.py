@@ -115,6 +115,27 @@ def test_prefill_validation(lib):
     assert _prefill(lib, ws=FAKE + 4, ws_bytes=1 << 30) == E
 
 
+def test_prefill_noalloc_validation(lib):
+    """The allocation-free prefill validates like la_prefill, before any HIP call."""
+    E, U = la.LA_ERR_INVALID_ARG, la.LA_ERR_UNSUPPORTED
+
+    def call(**kw):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=la.LA_DTYPE_BF16, cu=FAKE, batch=2, T=10, max_seqlen=8,
+                 H=4, HK=4, d=128, pool=FAKE, P=4, slot=FAKE, tl=None, ts=None, slopes=FAKE, out=FAKE)
+        a.update(kw)
+        return lib.la_prefill_noalloc(a["q"], a["k"], a["v"], a["dtype"], a["cu"], a["batch"], a["T"],
+                                      a["max_seqlen"], a["H"], a["HK"], a["d"], a["pool"], a["P"], a["slot"],
+                                      a["tl"], a["ts"], a["slopes"], a["out"], None)
+
+    assert call(d=32) == U
+    assert call(q=None) == E
+    assert call(cu=None) == E
+    assert call(max_seqlen=-1) == E
+    assert call(HK=3) == E
+    assert call(pool=FAKE + 4) == E
+    assert "static scratch" in la.la_status_string(la.LA_ERR_NO_SCRATCH)
+
+
 def test_workspace_query_matches_the_documented_size(lib):
     """la_prefill_workspace_bytes: batch*H*(S + (S-1)*Q) head_dim^2 floats, S
     segments (as many as fill the compute units, at most 8 and at most
