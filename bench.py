@@ -55,7 +55,7 @@ STATE_BYTES = D * D * 4
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = {
-    "prefill_chunked_kernel": ["prefill_chunked.hip", "common.h"],
+    "prefill_chunked_kernel": ["prefill_chunked.hip", "common.h", "host_logic.h"],
     "recurrent_kernel<bf16>": ["recurrent.hip", "common.h"],
     "tree_kernel<bf16>": ["recurrent.hip", "common.h"],
 }
@@ -76,9 +76,10 @@ def source_sha256(kernel):
 
 
 def measured_traffic(kernel, workload):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    counts (profiles/traffic.json), or None when they were taken on a different
-    version of the kernel's source or workload."""
+    """HBM bytes per launch from the committed rocprofv3 counts of L2-to-memory
+    requests (profiles/traffic.json: read requests by size class, write
+    requests and their 64-byte share, scaled by a plain copy's counts), or None
+    when they were taken on a different version of the kernel's source."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
