@@ -153,7 +153,6 @@ __device__ __forceinline__ f32x4 mma(u16x8 a, u16x8 b, f32x4 c) {
 }
 
 __device__ __forceinline__ u16x8 lds8(const uint16_t *p) { return *reinterpret_cast<const u16x8 *>(p); }
-__device__ __forceinline__ u16x4 lds4(const uint16_t *p) { return *reinterpret_cast<const u16x4 *>(p); }
 // An 8-byte read that the compiler may not pair with another into a
 // ds_read2_b64: the two halves of such a pair go to the same 8-byte half of a
 // 16-byte unit in every lane, which is a 2-way bank conflict under any row
