@@ -69,3 +69,50 @@ def test_noalloc_unsplit_and_empty():
                           torch.empty_like(d["q"]), 0)
     torch.cuda.synchronize()
     assert np.array_equal(d["pool"].cpu().numpy().view(np.uint32), wl0.pool.view(np.uint32))
+
+
+def test_noalloc_and_workspace_prefill_in_a_hip_graph():
+    """Both split prefills captured in one HIP graph (the allocation-free one
+    needs no allocation at capture or replay; the other gets its workspace
+    before capture) and replayed three times with eager pool resets and output
+    scribbles between replays; every replay matches the oracle and the eager
+    results bit for bit."""
+    wl = W.make("noalloc-graph", "prefill", "bf16", 8, [17000, 300], 4, seed=2305, prefix=[True, True])
+    d1, d2 = device_inputs(wl), device_inputs(wl)
+    pool0 = d1["pool"].clone()
+    need = la.la_prefill_workspace_bytes(wl.batch, wl.total_tokens, wl.max_seqlen, wl.num_heads, 128)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o1, o2 = torch.empty_like(d1["q"]), torch.empty_like(d2["q"])
+
+    def step():
+        la.la_prefill_noalloc(d1["q"], d1["k"], d1["v"], d1["cu"], d1["pool"], d1["slot"], d1["slopes"], o1,
+                              wl.max_seqlen)
+        la.la_prefill(d2["q"], d2["k"], d2["v"], d2["cu"], d2["pool"], d2["slot"], d2["slopes"], o2,
+                      wl.max_seqlen, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    check_against_oracle(wl, o1, d1["pool"])
+    ref = [t.clone() for t in (o1, d1["pool"], o2, d2["pool"])]
+    _same(ref[0], ref[2], "eager out")
+    for p in (d1["pool"], d2["pool"]):
+        p.copy_(pool0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for p in (d1["pool"], d2["pool"]):
+            p.copy_(pool0)
+        o1.fill_(-1.0)
+        o2.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("noalloc out", "noalloc pool", "workspace out", "workspace pool"),
+                              (o1, d1["pool"], o2, d2["pool"]), ref):
+            _same(a, b, f"replay {rep}: {name}")
+        check_against_oracle(wl, o1, d1["pool"])
+        log(f"graph replay {rep} ok")
