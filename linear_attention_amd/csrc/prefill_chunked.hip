@@ -650,19 +650,44 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
     // unit n is staged by staging group n % 2
     auto stages = [](int n) { return kHelper && (n & 1) == HG; };
 
-    // prologue: V of chunk 0 and unit 0 in LDS, V of chunk 0 decayed; units 1
-    // and 2 in flight
+    // prologue: V of chunk 0 (also decayed) and unit 0 in LDS, units 1 and 2
+    // in flight.  Group 0 loads V of chunk 0 and unit 0 together and decays
+    // its own V rows in registers: the staging layout of a V tile is the
+    // swizzled layout v_off that the decay writes, so each lane's decayed
+    // unit lands where it holds the raw one.
     if (stages(0)) {
-        load_v(0);
-        store_v(0);
+        u16x8 v0[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const uint32_t r = static_cast<uint32_t>(v_row[u] < chunk_c(0) ? v_row[u] : chunk_c(0) - 1);
+            v0[u] = *reinterpret_cast<const u16x8 *>(jb.v + chunk_t(0) * jb.kvrow + jb.kvcol + col0 +
+                                                     (r * kvrow + 8 * v_unit[u]));
+        }
         load_unit(0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int pos = 512 * (2 * HI + u) + 8 * lane;
+            const float vdec = nchunks == 1 ? (v_row[u] < c_last ? expf(-lam * (static_cast<float>(c_last - 1 - v_row[u]) + vshift)) : 0.f)
+                                            : expf(-lam * (static_cast<float>(C - 1 - v_row[u]) + vshift));
+            f32x4 x0, x1;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                x0[k] = bf16_to_f32(v0[u][k]) * vdec;
+                x1[k] = bf16_to_f32(v0[u][4 + k]) * vdec;
+            }
+            u16x4 h0, l0, h1, l1;
+            split4(x0, h0, l0);
+            split4(x1, h1, l1);
+            *reinterpret_cast<u16x8 *>(&sm.v[0][pos]) = v0[u];
+            *reinterpret_cast<u16x8 *>(&sm.vd_hi[0][pos]) = cat(h0, h1);
+            *reinterpret_cast<u16x8 *>(&sm.vd_lo[0][pos]) = cat(l0, l1);
+        }
         store_unit(0);
     }
     for (int n = 1; n <= 2; ++n)
         if (n < nchunks && stages(n)) load_unit(n);
     __syncthreads();
-    if constexpr (kHelper)
-        if (HG == 1) decay_v(0);
 
     for (int ci = 0; ci < nchunks; ++ci) {
         const bool last = ci + 1 == nchunks;
@@ -782,25 +807,38 @@ __device__ __forceinline__ void request_range(const PrefillArgs &a, int b, int64
 // was dispatched late.  Every workgroup ranks the (at most kSortMax) lengths
 // itself; the results do not depend on the order.
 constexpr int kSortMax = 256;
-__device__ __forceinline__ int request_of_rank(const PrefillArgs &a, int batch, int r, int *lens, int *pick) {
+struct Ranked {
+    int64_t t0[kSortMax];   // each request's range and slot, kept from the ranking
+    int64_t len[kSortMax];  // pass so that the picked one needs no second read
+    int slot[kSortMax];
+    int pick;
+};
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(x) >> 32));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ int request_of_rank(const PrefillArgs &a, int batch, int r, Ranked &rk) {
     const int tid = threadIdx.x;
     for (int i = tid; i < batch; i += NT) {
         int64_t t0, t1;
         request_range(a, i, t0, t1);
-        lens[i] = static_cast<int>(t1 - t0);
+        rk.t0[i] = t0;
+        rk.len[i] = t1 - t0;
+        rk.slot[i] = a.slot_idx[i];
     }
     __syncthreads();
     if (tid < batch) {
-        const int li = lens[tid];
+        const int64_t li = rk.len[tid];
         int rank = 0;
         for (int j = 0; j < batch; ++j) {
-            const int lj = lens[j];
+            const int64_t lj = rk.len[j];
             rank += (lj > li || (lj == li && j < tid)) ? 1 : 0;
         }
-        if (rank == r) *pick = tid;
+        if (rank == r) rk.pick = tid;
     }
     __syncthreads();
-    return *pick;
+    return rk.pick;
 }
 
 // Sequence segments.  A launch whose (request, head, column block) units
@@ -848,8 +886,7 @@ __device__ __forceinline__ void subseg_range(int cps, int subsegs, int q, int &c
 template <int D> __global__ __launch_bounds__(NT) void prefill_chunked_kernel(PrefillArgs a) {
     using G = Geo<D>;
     __shared__ Smem<D> sm;
-    __shared__ int sort_lens[kSortMax];
-    __shared__ int sort_pick;
+    __shared__ Ranked ranked;
 
     const int H = a.num_heads;
     const int units = a.pairs * G::NVB;
@@ -860,11 +897,20 @@ template <int D> __global__ __launch_bounds__(NT) void prefill_chunked_kernel(Pr
     int b = pair / H;
     const int h = pair - b * H;
     const int tid = threadIdx.x;
-    if (batch > 1 && batch <= kSortMax) b = request_of_rank(a, batch, b, sort_lens, &sort_pick);
-
-    int64_t t0, t1;
-    request_range(a, b, t0, t1);
-    int64_t len = t1 - t0;
+    int64_t t0, len;
+    int slot;
+    if (batch > 1 && batch <= kSortMax) {
+        // the picked request is the same for the whole workgroup: keep it scalar
+        b = __builtin_amdgcn_readfirstlane(request_of_rank(a, batch, b, ranked));
+        t0 = uniform64(ranked.t0[b]);
+        len = uniform64(ranked.len[b]);
+        slot = __builtin_amdgcn_readfirstlane(ranked.slot[b]);
+    } else {
+        int64_t t1;
+        request_range(a, b, t0, t1);
+        len = t1 - t0;
+        slot = a.slot_idx[b];
+    }
     const bool segmented = a.segments > 1;
     int nseg = 1;
     if (segmented) {
@@ -879,7 +925,6 @@ template <int D> __global__ __launch_bounds__(NT) void prefill_chunked_kernel(Pr
     const size_t row = static_cast<size_t>(H) * D;
     const size_t hcol = static_cast<size_t>(h) * D;
     const int col0 = vb * VB;
-    const int slot = a.slot_idx[b];
     if (slot < 0 || slot >= a.pool_slots) {
         // out-of-range slot: zero output for this column block, no state touched
         for (int64_t idx = tid; idx < len * (VB / 8); idx += NT) {
