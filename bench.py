@@ -65,13 +65,45 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def code_text(src):
+    """C/C++ source without its comments and with every run of white space
+    made one blank: the part of a file that can change the compiled kernel,
+    so that editing a comment does not detach the committed counters."""
+    out, i, n, in_str = [], 0, len(src), False
+    while i < n:
+        c = src[i]
+        if in_str:
+            out.append(c)
+            if c == "\\" and i + 1 < n:
+                out.append(src[i + 1])
+                i += 2
+                continue
+            in_str = c != '"'
+            i += 1
+        elif c == '"':
+            in_str = True
+            out.append(c)
+            i += 1
+        elif src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_sha256(kernel):
+    """sha256 of the code (code_text) of the kernel's source files, in order."""
     import hashlib
 
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(ROOT, "linear_attention_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "linear_attention_amd", "csrc", name), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode("utf-8"))
     return h.hexdigest()
 
 

@@ -49,9 +49,11 @@
 // in registers writes it to LDS, where the next barrier publishes it, and then
 // loads unit i + 3 into the same registers, two chunk times before they are
 // written.  Each wave has at most one unit of loads in flight, so vmcnt(0)
-// before the write waits for exactly that unit.  (Copying global memory straight into LDS was slower
-// once made safe: those copies do not complete in issue order, and copies
-// left in flight across a barrier gave stale tiles under load.)  Operands that
+// before the write waits for exactly that unit; the first chunk's V and unit 0
+// are loaded together behind one wait.  (Copying global memory straight into
+// LDS was slower once made safe: those copies do not complete in issue order,
+// and copies left in flight across a barrier gave stale tiles under load.)
+// Operands that
 // the MFMA needs with tokens along the contraction (K^T, V^T, Vd) are read
 // from the token-major tiles with ds_read_b64_tr_b16, whose 16-lane groups
 // return the columns of a 4-row block.  Tile rows are XOR-swizzled in
@@ -167,12 +169,10 @@ __device__ __forceinline__ u16x4 lds4_single(const uint16_t *p) {
 // columns col0 .. col0+15 (col0 a multiple of 16); lane (g, i) receives
 // column col0 + i of those four rows.
 //
-// The read is issued as inline assembly: the compiler cannot tell these LDS
-// reads apart from the in-flight global->LDS copies into other staging slots
-// and would otherwise wait for every outstanding copy before each of them.
-// The caller publishes the results with lds_fence(): a wait on the LDS
-// counter followed by an empty asm per value, which orders every consumer
-// after the wait.  (LDS operations complete in order, so the extra
+// The read is issued as inline assembly, so the compiler does not track when
+// its result arrives.  The caller waits with lds_wait() (a wait on the LDS
+// counter) and then pin()s each value, an empty asm that orders every
+// consumer after the wait.  (LDS operations complete in order, so the extra
 // outstanding reads only make the compiler's own LDS waits more conservative.)
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const lds_void *)p));

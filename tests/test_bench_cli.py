@@ -39,3 +39,25 @@ def test_useful_flops_per_token_head():
     # 4 d^2 (state update and inter term) + 2 C d (causal-half intra term), C = 64
     assert b.prefill_useful_flops(1, 1) == 4 * 128 * 128 + 2 * 64 * 128
     assert b.prefill_useful_flops(131072, 64) == 131072 * 64 * 81920
+
+
+def test_code_text_drops_comments_and_spacing_only():
+    b = _bench_module()
+    src = 'int a = 1; // note\n/* block\n   comment */  const char *s = "x // y \\" z";\n\tint  b;\n'
+    assert b.code_text(src) == 'int a = 1; const char *s = "x // y \\" z"; int b;'
+    # a comment or layout edit keeps the digest, a code edit changes it
+    assert b.code_text("x = y + 1; // one") == b.code_text("x = y + 1;   /* other */")
+    assert b.code_text("x = y + 1;") != b.code_text("x = y + 2;")
+
+
+def test_committed_traffic_entries_are_well_formed():
+    import json
+    b = _bench_module()
+    t = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))
+    assert 0.99 < t["copy_read_scale"] < 1.01 and 0.99 < t["copy_write_scale"] < 1.01
+    for kernel in b.KERNEL_SOURCES:
+        for workload, e in t[kernel].items():
+            assert len(e["source_sha256"]) == 64, (kernel, workload)
+            assert e["traffic_bytes"] == e["read_bytes"] + e["write_bytes"]
+            assert e["read_bytes"] > 0 and e["write_bytes"] > 0
+            assert e["traffic_bytes"] >= 0.99 * e["algorithmic_bytes"], (kernel, workload)
