@@ -14,6 +14,8 @@ Every output and final state is checked against the fp64 oracle, and every
 pool slot a call must not write is compared bit for bit.  The case's
 configuration is printed before it runs.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -25,6 +27,16 @@ from linear_attention_amd import workloads as W
 from gpu_util import TOL, assert_close, check_against_oracle, check_untouched, device_inputs, host_io, log, run_gpu
 
 pytestmark = pytest.mark.gpu
+
+
+def _seeds(default):
+    """Seeds of the random cases: range(default), or range(a, a + n) when the
+    environment sets LA_RANDOM_SEEDS=a:n (for a longer campaign)."""
+    spec = os.environ.get("LA_RANDOM_SEEDS")
+    if not spec:
+        return range(default)
+    a, n = (int(x) for x in spec.split(":"))
+    return range(a, a + n)
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -75,7 +87,7 @@ def _config(seed):
     return wl, state_out
 
 
-@pytest.mark.parametrize("seed", range(60))
+@pytest.mark.parametrize("seed", _seeds(60))
 def test_random_configuration(seed):
     wl, state_out = _config(seed)
     log(f"case {wl.name}: {wl.kind} {wl.dtype} B={wl.batch} H={wl.num_heads} HK={wl.num_kv_heads} "
@@ -94,7 +106,7 @@ def _small_config(rng):
     return dtype, d, H, H // int(rng.choice(groups))
 
 
-@pytest.mark.parametrize("seed", range(20))
+@pytest.mark.parametrize("seed", _seeds(20))
 def test_random_tree(seed):
     """Tree verify with a random parent array per request: outputs and every
     per-position state against the oracle; the pool is never written."""
@@ -122,7 +134,7 @@ def test_random_tree(seed):
     assert_close(ds.cpu().numpy(), ref_states, TOL[dtype], f"{wl.name} draft states")
 
 
-@pytest.mark.parametrize("seed", range(20))
+@pytest.mark.parametrize("seed", _seeds(20))
 def test_random_track(seed):
     """Prefill with state snapshots: random snapshot points (0, mid-chunk, a
     chunk edge, the whole request), some requests without one, track slots
