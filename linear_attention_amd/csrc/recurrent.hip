@@ -15,6 +15,8 @@
 // groups of a wave with cross-lane shuffles and across the 4 waves in LDS.
 #include <type_traits>
 
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -159,7 +161,7 @@ __device__ __forceinline__ void decay_step(f32x4 &x, float dhi, f32x4 t) {
 // kTrack: the prefill variant that may take a state-tracking snapshot.
 // kMulti: requests of more than one token (without it every token is a group
 // of its own: decode, whose one-token body then needs fewer registers).
-template <typename T, int D, bool kTrack, bool kMulti>
+template <typename T, int D, bool kTrack, bool kMulti, bool kBatched>
 __global__ __launch_bounds__(kThreads) void recurrent_kernel(RecurrentArgs a) {
     using L = Layout<D>;
     constexpr int RPT = L::RPT;
@@ -233,6 +235,17 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(RecurrentArgs a) {
 
     __shared__ f32x4 red[2][4][L::CG];
     int parity = 0;
+    // the next token's k, q and v rows (fp32 several-token requests)
+    Row<T, RPT> kk_next, qq_next;
+    f32x4 vv_next;
+    auto fetch = [&](int64_t s) {
+        const size_t kvoff = s * kvrow + static_cast<size_t>(hk) * D;
+        kk_next.load(k + kvoff + RPT * rg);
+        qq_next.load(q + s * row + static_cast<size_t>(h) * D + RPT * rg);
+        vv_next = load4(v + kvoff + 4 * cg);
+    };
+    if constexpr (kBatched)
+        if (t0 < t1) fetch(t0);
     // one token; kFirst: the first of its group, which also applies the decay
     auto token = [&](int64_t s, int64_t e, float whi, float wlo, auto first) {
         constexpr bool kFirst = decltype(first)::value;
@@ -254,6 +267,69 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(RecurrentArgs a) {
         }
         reduce_store<D>(o, red, parity, out + off, L::kScale * expf(lam * static_cast<float>(e - s)));
     };
+    // One group of G <= kGroup tokens from t (fp32 several-token requests).
+    auto group = [&](int64_t t, int G, float whi, float wlo) {
+        if constexpr (kBatched) {
+            __shared__ f32x4 redg[2][4][kGroup][L::CG];
+            static_assert(sizeof(redg) <= 32768, "group reduction buffer");
+            f32x4 po[kGroup];
+#pragma unroll
+            for (int i = 0; i < kGroup; ++i) {
+                if (i < G) {
+                    const int64_t s = t + i;
+                    const float w = expf(-lam * static_cast<float>(G - 1 - i));
+                    const Row<T, RPT> kk = kk_next, qq = qq_next;
+                    const f32x4 vv = vv_next;
+                    if (s + 1 < t1) fetch(s + 1);
+                    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int r = 0; r < RPT; ++r) {
+                        if (i == 0)
+                            decay_step(S[r], whi, wlo * S[r] + (w * kk[r]) * vv);
+                        else
+                            S[r] += (w * kk[r]) * vv;
+                        o += qq[r] * S[r];
+                    }
+                    po[i] = o;
+                }
+            }
+            const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+            for (int i = 0; i < kGroup; ++i) {
+                if (i < G) {
+#pragma unroll
+                    for (int m = L::CG; m < 64; m <<= 1) {
+                        po[i].x += __shfl_xor(po[i].x, m);
+                        po[i].y += __shfl_xor(po[i].y, m);
+                        po[i].z += __shfl_xor(po[i].z, m);
+                        po[i].w += __shfl_xor(po[i].w, m);
+                    }
+                    if (lane < L::CG) redg[parity][wave][i][cg] = po[i];
+                }
+            }
+            __syncthreads();
+            if (wave == 0 && lane < L::CG) {
+#pragma unroll
+                for (int i = 0; i < kGroup; ++i) {
+                    if (i < G) {
+                        const f32x4 sum = redg[parity][0][i][lane] + redg[parity][1][i][lane] +
+                                          redg[parity][2][i][lane] + redg[parity][3][i][lane];
+                        const size_t off = (t + i) * row + static_cast<size_t>(h) * D;
+                        store4(out + off + 4 * lane, sum * (L::kScale * expf(lam * static_cast<float>(G - 1 - i))));
+                    }
+                }
+            }
+            parity ^= 1;
+        }
+    };
+    // kBatched (fp32 prefill): the partial outputs of a group's tokens are
+    // reduced across the row groups together, one barrier per group instead
+    // of one per token, and each token's inputs are fetched while the one
+    // before is computed.  Same arithmetic, in the same order, as the
+    // token-at-a-time body above, which chain verify keeps: its requests are
+    // a few tokens each, and the extra registers and LDS would cost it
+    // occupancy (fp32 verify measured 4% slower with it).
+    static_assert(!kBatched || (kMulti && std::is_same<T, float>::value), "batched groups: fp32, several tokens");
     for (int64_t t = t0; t < t1;) {
         int64_t G = t1 - t < gmax ? t1 - t : gmax;
         if (kTrack && snap) {
@@ -264,9 +340,13 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(RecurrentArgs a) {
         const int64_t e = t + G - 1;
         const float whi = expf(-lam * static_cast<float>(G));
         const float wlo = whi >= 0.5f ? expm1f(-lam * static_cast<float>(G)) - (whi - 1.f) : 0.f;
-        token(t, e, whi, wlo, std::true_type{});
-        if constexpr (kMulti)
-            for (int64_t s = t + 1; s <= e; ++s) token(s, e, whi, wlo, std::false_type{});
+        if constexpr (kBatched) {
+            group(t, static_cast<int>(G), whi, wlo);
+        } else {
+            token(t, e, whi, wlo, std::true_type{});
+            if constexpr (kMulti)
+                for (int64_t s = t + 1; s <= e; ++s) token(s, e, whi, wlo, std::false_type{});
+        }
         t = e + 1;
     }
     if (kTrack && snap && tl == t1 - t0) store_state<D>(snap, soff, S);
@@ -386,9 +466,14 @@ hipError_t launch_rec(const RecurrentArgs &a, int batch, hipStream_t stream) {
     RecurrentArgs copy = a;
     void *args[] = {&copy};
     const bool one = !a.cu_seqlens && a.tokens_per_req == 1;  // decode
-    const void *fn = a.track_lens ? reinterpret_cast<const void *>(&recurrent_kernel<T, D, true, true>)
-                     : one        ? reinterpret_cast<const void *>(&recurrent_kernel<T, D, false, false>)
-                                  : reinterpret_cast<const void *>(&recurrent_kernel<T, D, false, true>);
+    const void *fn = a.track_lens ? reinterpret_cast<const void *>(&recurrent_kernel<T, D, true, true, false>)
+                     : one        ? reinterpret_cast<const void *>(&recurrent_kernel<T, D, false, false, false>)
+                                  : reinterpret_cast<const void *>(&recurrent_kernel<T, D, false, true, false>);
+    if constexpr (std::is_same<T, float>::value) {
+        if (a.cu_seqlens)  // fp32 prefill (with or without a snapshot): groups reduced together
+            fn = a.track_lens ? reinterpret_cast<const void *>(&recurrent_kernel<T, D, true, true, true>)
+                              : reinterpret_cast<const void *>(&recurrent_kernel<T, D, false, true, true>);
+    }
     return hipLaunchKernel(fn,
                            dim3(static_cast<unsigned>(batch) * a.num_heads), dim3(kThreads), args,
                            0, stream);
