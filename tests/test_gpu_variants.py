@@ -178,11 +178,13 @@ def test_head_dim_64_long_prefill_sampled_heads():
 # ---------------------------------------------------------------- slope regimes, invalid slots
 
 # slopes in [0, 2] take the chunked kernel's scaled-state decay, larger ones
-# its explicit per-token weights
-SLOPES = [0.0, 1e-3, 0.25, 2.0, 2.0001, 3.0, 8.0, 0.9]
+# its explicit per-token weights; in the token-recurrent kernel (fp32) the
+# decay groups shrink as the slope grows (8 tokens up to 32/7, 5 at 8, one
+# token at 40)
+SLOPES = [0.0, 1e-3, 0.25, 2.0, 2.0001, 3.0, 8.0, 0.9, 40.0]
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp32", 64)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("fp32", 64), ("fp32", 128)])
 def test_prefill_slopes_on_both_sides_of_two(dtype, d):
     lens = [1, 64, 65, 200, 130]
     H = len(SLOPES)
