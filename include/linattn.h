@@ -44,8 +44,9 @@
  * Calls are asynchronous on `stream` (0 = the null stream): the library does
  * no host synchronisation, no device-to-host reads and no allocation, and
  * keeps no state between calls (beyond each device's compute-unit count,
- * read once).  Scratch memory, where a call can use it, is the caller's:
- * see la_prefill_workspace_bytes.  The inputs must not alias out, state_pool,
+ * read once, and the static scratch of la_prefill_noalloc).  Scratch memory,
+ * where a call can use it, is otherwise the caller's: see
+ * la_prefill_workspace_bytes.  The inputs must not alias out, state_pool,
  * state_out or the workspace.  Overlapping calls that name the same pool slot
  * or share a workspace race.
  *
@@ -141,7 +142,8 @@ size_t la_prefill_workspace_bytes(int batch, int64_t total_tokens, int max_seqle
  * Track slots must be distinct from each other and from every slot_idx entry.
  *
  * bf16 (d = 64 or 128): chunked MFMA kernel (fp32 state, bf16 hi/lo operand
- * splits).  fp32: token-recurrent fp32 kernel.
+ * splits).  fp32: token-recurrent fp32 kernel, one workgroup per (request,
+ * head), the outputs of each group of up to 8 tokens reduced together.
  *
  * workspace, workspace_bytes: device scratch owned by the caller, 16-byte
  * aligned, used only by a call that splits into sequence segments (see
