@@ -668,8 +668,10 @@ __device__ __forceinline__ void run_wave(Smem<D> &sm, const Job &jb) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int pos = 512 * (2 * HI + u) + 8 * lane;
-            const float vdec = nchunks == 1 ? (v_row[u] < c_last ? expf(-lam * (static_cast<float>(c_last - 1 - v_row[u]) + vshift)) : 0.f)
-                                            : expf(-lam * (static_cast<float>(C - 1 - v_row[u]) + vshift));
+            const float vdec =
+                nchunks == 1
+                    ? (v_row[u] < c_last ? expf(-lam * (static_cast<float>(c_last - 1 - v_row[u]) + vshift)) : 0.f)
+                    : expf(-lam * (static_cast<float>(C - 1 - v_row[u]) + vshift));
             f32x4 x0, x1;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {

@@ -15,8 +15,6 @@
 // groups of a wave with cross-lane shuffles and across the 4 waves in LDS.
 #include <type_traits>
 
-#include <type_traits>
-
 #include "common.h"
 #include "launch.h"
 
