@@ -266,16 +266,27 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(RecurrentArgs a) {
         reduce_store<D>(o, red, parity, out + off, L::kScale * expf(lam * static_cast<float>(e - s)));
     };
     // One group of G <= kGroup tokens from t (fp32 several-token requests).
+    // weights e^{-l d} and output factors e^{l d} of a full group (d = 0..7),
+    // computed once per call (a partial group computes its own)
+    float wfull[kGroup], ofull[kGroup];
+    if constexpr (kBatched) {
+#pragma unroll
+        for (int d = 0; d < kGroup; ++d) {
+            wfull[d] = expf(-lam * static_cast<float>(d));
+            ofull[d] = L::kScale * expf(lam * static_cast<float>(d));
+        }
+    }
     auto group = [&](int64_t t, int G, float whi, float wlo) {
         if constexpr (kBatched) {
             __shared__ f32x4 redg[2][4][kGroup][L::CG];
+            const bool full = G == kGroup;
             static_assert(sizeof(redg) <= 32768, "group reduction buffer");
             f32x4 po[kGroup];
 #pragma unroll
             for (int i = 0; i < kGroup; ++i) {
                 if (i < G) {
                     const int64_t s = t + i;
-                    const float w = expf(-lam * static_cast<float>(G - 1 - i));
+                    const float w = full ? wfull[kGroup - 1 - i] : expf(-lam * static_cast<float>(G - 1 - i));
                     const Row<T, RPT> kk = kk_next, qq = qq_next;
                     const f32x4 vv = vv_next;
                     if (s + 1 < t1) fetch(s + 1);
@@ -313,7 +324,9 @@ __global__ __launch_bounds__(kThreads) void recurrent_kernel(RecurrentArgs a) {
                         const f32x4 sum = redg[parity][0][i][lane] + redg[parity][1][i][lane] +
                                           redg[parity][2][i][lane] + redg[parity][3][i][lane];
                         const size_t off = (t + i) * row + static_cast<size_t>(h) * D;
-                        store4(out + off + 4 * lane, sum * (L::kScale * expf(lam * static_cast<float>(G - 1 - i))));
+                        const float oscale =
+                            full ? ofull[kGroup - 1 - i] : L::kScale * expf(lam * static_cast<float>(G - 1 - i));
+                        store4(out + off + 4 * lane, sum * oscale);
                     }
                 }
             }
