@@ -173,6 +173,9 @@ def prefill_variants(ms, ms_min, T, H):
                       "hbm_frac": tp8_bytes / (ms["prefill_tp8"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
                       "unsegmented_avg_ms": ms["prefill_tp8_unseg"],
                       "segment_speedup": ms["prefill_tp8_unseg"] / ms["prefill_tp8"]},
+        "fp32": {"workload": f"prefill T={T64} H={H} d={D} fp32 (token-recurrent kernel, one workgroup per head)",
+                 "avg_ms": ms["prefill_fp32"], "min_ms": ms_min["prefill_fp32"],
+                 "tokens_per_s": T64 / (ms["prefill_fp32"] * 1e-3)},
     }
 
 
@@ -469,9 +472,19 @@ def main():
             # no workspace: the call runs unsplit
             return lambda: fn(ws=None)
 
+        # fp32 inputs (the same values, upcast exactly): the token-recurrent kernel
+        V4.update({"q32": P["q"][:T64].float(), "k32": P["k"][:T64].float(), "v32": P["v"][:T64].float(),
+                   "pool32": torch.zeros((2, 64, D, D), device=dev)})
+        V4["out32"] = torch.empty_like(V4["q32"])
+
+        def run_fp32():
+            la.la_prefill(V4["q32"], V4["k32"], V4["v32"], V4["cu64"], V4["pool32"], P["slot"], P["slopes"],
+                          V4["out32"], T64, workspace=None, stream=stream)
+
         extra += [("prefill_track", run_track), ("prefill_gqa", run_gqa), ("prefill_d64", run_d64),
                   ("prefill_varlen", run_varlen), ("prefill_tp8", run_tp8),
-                  ("prefill_tp8_unseg", unsegmented(run_tp8)), ("prefill_d64_unseg", unsegmented(run_d64))]
+                  ("prefill_tp8_unseg", unsegmented(run_tp8)), ("prefill_d64_unseg", unsegmented(run_d64)),
+                  ("prefill_fp32", run_fp32)]
         V4["varlen"] = w2
     for _ in range(args.warmup):
         for _, fn in calls + extra:
