@@ -15,6 +15,10 @@ by the sub-ulp decay alone, and no round-to-nearest form of the step gives
 the exact rate (a per-step decay of 0.3-0.7 ulp rounds to 0 or 1 ulp).  Where
 |S| >> 256 |k v| the update lands at effectively random positions within an
 ulp, the rounding is unbiased, and the pair must reproduce e^{-l n} exactly.
+Pure decay (k = 0) is the extreme of the first regime: a step that only
+decays moves the state by a fraction of an ulp, which rounds to a whole
+number of ulps, so no fp32 state can follow e^{-l n} to 1e-6 there; the
+second regime is where that accuracy is pinned.
 
 Both regimes are checked against the fp64 oracle over 1000 decode steps and
 200 verify calls of 5 drafts:
