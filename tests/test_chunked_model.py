@@ -8,11 +8,13 @@ steps is exact algebra, so in fp64 the model must reproduce the oracle to
 rounding: this checks the algebra on the CPU, apart from the kernel's bf16
 operand rounding, which the GPU parity tests bound.  Chunk lengths 1, 7, 64
 and 128, slopes on both sides of the frame's limit, lengths at chunk and
-segment edges.  ([LA-page]: the page "SGLang Lightning Attention 能力矩阵与
-seg_la 线性注意力测试覆盖深度解析", www.2kiu.com/news/4599301.)
+segment edges, and 200 drawn decompositions (hypothesis, derandomized).
+([LA-page]: the page "SGLang Lightning Attention 能力矩阵与 seg_la
+线性注意力测试覆盖深度解析", www.2kiu.com/news/4599301.)
 """
 import numpy as np
 import pytest
+from hypothesis import given, settings, strategies as st
 
 import oracle
 from chunked_model import frame_center, prefill, segment_geometry
@@ -118,3 +120,23 @@ def test_frame_factors_stay_in_float32_range_for_64_token_chunks():
             small = vw[~((vw > f32.tiny) & (vw < f32.max))]
             fits &= bool(small.size == 0 or small.max() / vw.max() < 1e-10)
         assert fits == ok, C
+
+
+@settings(max_examples=200, deadline=None, derandomize=True)
+@given(n=st.integers(1, 260), C=st.sampled_from([1, 3, 7, 16, 64, 100, 128]),
+       lam=st.one_of(st.floats(0.0, 2.0), st.floats(2.0, 12.0)),
+       segments=st.integers(1, 8), subsegs=st.integers(1, 4), d=st.sampled_from([4, 16]),
+       seed=st.integers(0, 2**16))
+def test_random_decompositions_equal_recurrence(n, C, lam, segments, subsegs, d, seed):
+    """Drawn chunk lengths, slopes on both sides of the frame's limit, request
+    lengths and segment/sub-segment splits: the decomposition equals the
+    per-token recurrence in fp64.  (The scaled frame is only ever used with
+    C = 64 by the kernel; at larger C and slopes its factors leave the fp64
+    range too, so it is drawn only where they stay inside it.)"""
+    lam32 = float(np.float32(lam))
+    factored = 0.0 <= lam32 <= 2.0 and lam32 * C < 600
+    q, k, v, S0 = _inputs(n, d, seed)
+    got_o, got_s = prefill(q, k, v, S0, lam32, C=C, segments=segments, subsegs=subsegs, factored=factored)
+    ref_o, ref_s = _oracle(q, k, v, S0, lam32)
+    _close(got_o, ref_o, f"n={n} C={C} lam={lam32} S={segments} Q={subsegs} out")
+    _close(got_s, ref_s, f"n={n} C={C} lam={lam32} S={segments} Q={subsegs} state")
